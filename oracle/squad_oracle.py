@@ -1,0 +1,241 @@
+"""Oracle for SQuad-Attention: a plain, slow, float64 CPU statement of the operator.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the HIP
+library and its Python binding) never calls it and shares no code with it.
+
+What is computed, and where the pages define it
+-----------------------------------------------
+Source pages (all titled "SQuad: Sub-Quadratic Attention Distillation for Efficient
+Video Generation"):
+
+* gist.science, technical summary ("Technische Samenvatting"), section
+  "Methodologie: SQuad", item "1. SQuad-Attention Operator":
+    - Local Pass Attn_L: tokens mix inside fixed windows of size w.
+    - Global Pass Attn_G: tokens that sit at the same relative position inside
+      their window mix across all windows.
+    - Composition: the local pass's output is the value stream of the global pass.
+    - Complexity: w = sqrt(n) gives O(n sqrt n); both passes use the standard
+      softmax.
+* the abstract (arxivdaily.com and the arXiv listing): self-attention over the n
+  latent tokens of a video DiT, softmax(QK^T); the distilled attention has no
+  extra learnable parameters (gist.science, "Experimentele Resultaten").
+
+Readings taken where the pages are silent (each one is also listed in the design
+notes of this repository):
+
+* Tokens are the cells of a T x H x W latent grid, flattened row-major over
+  (t, h, w).  A window is a tt x th x tw tile of that grid; the grid must be a
+  whole number of tiles.  Windows are numbered row-major over the window grid
+  (T/tt, H/th, W/tw); the relative position (offset) of a token inside its window
+  is numbered row-major over (tt, th, tw).  Only the partitions matter: attention
+  is permutation-equivariant inside a window and inside an offset group.
+* The global pass uses the same q and k as the local pass (there are no extra
+  parameters), with v replaced by the local output; out = Attn_G(q, k, Attn_L(q, k, v)).
+  Nothing is added to it (no residual, gate or sum).
+* Softmax scale s = 1/sqrt(d) in both passes unless the caller gives another;
+  softmax is taken in its max-subtracted form.
+* Batch elements and heads are independent; there is no mask and no causality.
+
+All arithmetic is float64.  Every function below is written from the definition,
+with numpy fancy indexing and numpy matmul as its only library steps.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "window_index",
+    "softmax_attention",
+    "local_pass",
+    "global_pass",
+    "squad_forward",
+    "squad_forward_groups",
+    "dense_attention",
+    "tile_gather",
+    "tile_scatter",
+    "window_to_group",
+    "window_attn",
+]
+
+
+def _check_grid(grid, tile):
+    T, H, W = (int(x) for x in grid)
+    tt, th, tw = (int(x) for x in tile)
+    if min(T, H, W, tt, th, tw) <= 0:
+        raise ValueError("grid and tile sizes must be positive")
+    if T % tt or H % th or W % tw:
+        raise ValueError(f"grid {grid} is not a whole number of {tile} tiles")
+    return T, H, W, tt, th, tw
+
+
+def window_index(grid, tile) -> np.ndarray:
+    """Token index of every (window, offset) pair: an int64 array idx[G, Wn].
+
+    idx[g, p] is the row-major (t, h, w) token index of the token at relative
+    position p inside window g.  Windows are the "fixed windows of size w" of the
+    local pass; row p of idx.T is the set of tokens "at the same relative position
+    within each window" that the global pass mixes (gist.science technical
+    summary, Methodologie, "1. SQuad-Attention Operator").
+    """
+    T, H, W, tt, th, tw = _check_grid(grid, tile)
+    tok = np.arange(T * H * W, dtype=np.int64).reshape(T, H, W)
+    # split each axis into (window coordinate, coordinate inside the window)
+    tok = tok.reshape(T // tt, tt, H // th, th, W // tw, tw)
+    # windows row-major over (T/tt, H/th, W/tw), offsets row-major over (tt, th, tw)
+    tok = tok.transpose(0, 2, 4, 1, 3, 5)
+    return tok.reshape((T // tt) * (H // th) * (W // tw), tt * th * tw).copy()
+
+
+def softmax_attention(q, k, v, scale) -> np.ndarray:
+    """Standard softmax attention over the last two axes, in float64.
+
+    q: [..., Lq, d], k: [..., Lk, d], v: [..., Lk, dv].  Row i of the result is
+    sum_j a_ij v_j with a_ij = exp(l_ij - max_j l_ij) / sum_j exp(l_ij - max_j l_ij)
+    and l_ij = scale * <q_i, k_j>.  Both passes of the operator use this standard
+    softmax (gist.science technical summary, "1. SQuad-Attention Operator",
+    Complexiteit).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    logits = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
+    logits = logits - logits.max(axis=-1, keepdims=True)
+    w = np.exp(logits)
+    w = w / w.sum(axis=-1, keepdims=True)
+    return np.matmul(w, v)
+
+
+def _default_scale(d, scale):
+    return 1.0 / np.sqrt(d) if scale is None or scale <= 0 else float(scale)
+
+
+def _as_bnhd(x, name):
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 4:
+        raise ValueError(f"{name} must be [batch, n, heads, head_dim]")
+    return x
+
+
+def local_pass(q, k, v, grid, tile, scale=None) -> np.ndarray:
+    """Attn_L: softmax attention inside each window.  [B, n, Hh, d] -> [B, n, Hh, d].
+
+    gist.science technical summary, "1. SQuad-Attention Operator", Local Pass.
+    """
+    q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
+    idx = window_index(grid, tile)                      # [G, Wn]
+    s = _default_scale(q.shape[-1], scale)
+    # [B, G, Wn, Hh, d] -> [B, Hh, G, Wn, d]
+    qw = q[:, idx].transpose(0, 3, 1, 2, 4)
+    kw = k[:, idx].transpose(0, 3, 1, 2, 4)
+    vw = v[:, idx].transpose(0, 3, 1, 2, 4)
+    ow = softmax_attention(qw, kw, vw, s)               # [B, Hh, G, Wn, d]
+    o = np.empty_like(v)
+    o[:, idx] = ow.transpose(0, 2, 3, 1, 4)
+    return o
+
+
+def global_pass(q, k, v, grid, tile, scale=None) -> np.ndarray:
+    """Attn_G: softmax attention among the tokens sharing one offset, across windows.
+
+    gist.science technical summary, "1. SQuad-Attention Operator", Global Pass.
+    Here v is the value stream, which in the operator is the local pass's output.
+    """
+    q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
+    grp = window_index(grid, tile).T                    # [Wn, G]: group p = tokens at offset p
+    s = _default_scale(q.shape[-1], scale)
+    qg = q[:, grp].transpose(0, 3, 1, 2, 4)             # [B, Hh, Wn, G, d]
+    kg = k[:, grp].transpose(0, 3, 1, 2, 4)
+    vg = v[:, grp].transpose(0, 3, 1, 2, 4)
+    og = softmax_attention(qg, kg, vg, s)
+    o = np.empty_like(v)
+    o[:, grp] = og.transpose(0, 2, 3, 1, 4)
+    return o
+
+
+def squad_forward(q, k, v, grid, tile, scale=None) -> np.ndarray:
+    """SQuad-Attention forward: out = Attn_G(q, k, Attn_L(q, k, v)).
+
+    The local output feeds the value stream of the global pass (gist.science
+    technical summary, "1. SQuad-Attention Operator", Compositie).
+    """
+    o1 = local_pass(q, k, v, grid, tile, scale)
+    return global_pass(q, k, o1, grid, tile, scale)
+
+
+def squad_forward_groups(q, k, v, grid, tile, offsets, scale=None):
+    """Rows of squad_forward for the chosen offset groups only.
+
+    For offset p the global pass needs the local output only at the tokens of
+    group p, and each of those is one query row of a local-pass window.  This
+    computes exactly those rows, then the global pass over each chosen group; it
+    is the same definition restricted to a subset of outputs, used to check
+    full-size results by sampling.
+
+    Returns (tokens [P, G] int64, out [B, P, G, Hh, d]) where tokens[i, g] is the
+    token index of window g's member of group offsets[i].
+    """
+    q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
+    idx = window_index(grid, tile)                      # [G, Wn]
+    offsets = np.asarray(offsets, dtype=np.int64).reshape(-1)
+    s = _default_scale(q.shape[-1], scale)
+    kw = k[:, idx].transpose(0, 3, 1, 2, 4)             # [B, Hh, G, Wn, d]
+    vw = v[:, idx].transpose(0, 3, 1, 2, 4)
+    tokens = idx[:, offsets].T.copy()                   # [P, G]
+    outs = []
+    for i, p in enumerate(offsets):
+        tok = tokens[i]                                 # [G]
+        qp = q[:, tok].transpose(0, 2, 1, 3)            # [B, Hh, G, d]
+        # local pass, one query row (the token at offset p) per window
+        o1p = softmax_attention(qp[:, :, :, None, :], kw, vw, s)[:, :, :, 0, :]
+        kp = k[:, tok].transpose(0, 2, 1, 3)
+        outp = softmax_attention(qp, kp, o1p, s)        # [B, Hh, G, d]
+        outs.append(outp.transpose(0, 2, 1, 3))         # [B, G, Hh, d]
+    return tokens, np.stack(outs, axis=1)
+
+
+def dense_attention(q, k, v, scale=None) -> np.ndarray:
+    """Full softmax self-attention over all n tokens, per batch element and head.
+
+    The quadratic operator the method replaces (abstract, all pages).
+    [B, n, Hh, d] -> [B, n, Hh, d].
+    """
+    q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
+    s = _default_scale(q.shape[-1], scale)
+    o = softmax_attention(q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3),
+                          v.transpose(0, 2, 1, 3), s)
+    return o.transpose(0, 2, 1, 3)
+
+
+# ---- the tensor reshapings the method is built from (gist.science technical
+# summary, "Belangrijkste Bijdragen": standard tensor reshaping and standard
+# attention blocks) ----
+
+def tile_gather(x, grid, tile) -> np.ndarray:
+    """Token order [B, n, Hh, d] -> window-major [B, Hh, G, Wn, d]."""
+    x = np.asarray(x)
+    idx = window_index(grid, tile)
+    return x[:, idx].transpose(0, 3, 1, 2, 4).copy()
+
+
+def tile_scatter(y, grid, tile) -> np.ndarray:
+    """Inverse of tile_gather: [B, Hh, G, Wn, d] -> token order [B, n, Hh, d]."""
+    y = np.asarray(y)
+    idx = window_index(grid, tile)
+    B, Hh, G, Wn, d = y.shape
+    out = np.empty((B, G * Wn, Hh, d), dtype=y.dtype)
+    out[:, idx] = y.transpose(0, 2, 3, 1, 4)
+    return out
+
+
+def window_to_group(y) -> np.ndarray:
+    """Window-major [B, Hh, G, Wn, d] -> offset-group-major [B, Hh, Wn, G, d]."""
+    return np.ascontiguousarray(np.asarray(y).transpose(0, 1, 3, 2, 4))
+
+
+def window_attn(q, k, v, scale=None) -> np.ndarray:
+    """Independent softmax attention per unit: [U, L, d] each -> [U, L, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    s = _default_scale(q.shape[-1], scale)
+    return softmax_attention(q, k, v, s)
