@@ -1,0 +1,271 @@
+"""Benchmark: SQuad-Attention forward on one MI355X.
+
+One step = one squad_attn_forward (local pass + global pass, with the window
+gather, the window-to-group regroup and the scatter folded into the two kernels'
+loads and stores) over the high-resolution workload: batch 1, 24 heads, head_dim
+128, latent grid 64x48x80 = 245,760 tokens, tile 4x12x10 (W = 480 tokens per
+window, G = 512 windows), bf16 q, k, v drawn i.i.d. N(0, 1) (seed 4), already
+resident in HBM when the timed region starts.
+
+Prints one JSON line.  `value` is tokens per second (batch * n / step time).
+Beside it: achieved TFLOP/s and the fraction of the bf16 dense MFMA peak, the
+roofline object of the dominant kernel (its average duration from HIP events on
+the launch stream), the float64 CPU oracle timed on a bounded sample of the same
+workload, and a dense full-attention comparator on the 5B-DiT-shaped workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "SQuad-attn tokens/s and TFLOP/s (% bf16 MFMA peak) at 1 MI355X"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="highres_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's timed sample")
+    return p.parse_args()
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "squad_map.h", "squad_kernels.h", "squad_api.hip"):
+        with open(os.path.join(ROOT, "sub_quadratic_windowed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, digest):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel source, if any."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, stream, iters):
+    """Average duration (ms) of fn() over iters launches, from HIP events on `stream`."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(cfg, qc, kc, vc, heads):
+    """The float64 oracle as it stands, on `heads` of the workload's heads."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    hs = list(range(heads))
+    q = qc[:, :, hs].double().numpy()
+    k = kc[:, :, hs].double().numpy()
+    v = vc[:, :, hs].double().numpy()
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    oracle.squad_forward(q, k, v, cfg.grid, cfg.tile)
+    dt = time.perf_counter() - t0
+    # tokens/s of the whole workload: the sample did heads/H of every token's work
+    value = cfg.batch * cfg.n * (heads / cfg.heads) / dt
+    return {
+        "value": value,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle, full forward over {heads} of {cfg.heads} heads "
+                  f"({cfg.batch}x{cfg.n} tokens, head_dim {cfg.head_dim}); {dt:.1f} s, scaled by "
+                  f"{cfg.heads}/{heads} to the whole workload",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the heads of SQuad-Attention "
+              "shard across GPUs with no exchange, so N GPUs would each run this workload's heads/N.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sub_quadratic_windowed_amd as sq
+    from sub_quadratic_windowed_amd import inputs
+
+    cfg = inputs.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    qc, kc, vc = inputs.config_inputs(cfg)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(sq.squad_attn_workspace_size(cfg.grid, cfg.tile, cfg.heads, cfg.batch, cfg.head_dim,
+                                                  cfg.dtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        sq.squad_attn_forward(q, k, v, cfg.grid, cfg.tile, cfg.heads, out=out, workspace=ws, stream=stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    print(f"[bench] {args.steps} steps, {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: each half of the forward alone, HIP events on the launch stream
+    local = lambda: sq.squad_attn_forward_local(q, k, v, cfg.grid, cfg.tile, cfg.heads, workspace=ws,
+                                                stream=stream)
+    glob = lambda: sq.squad_attn_forward_global(q, k, cfg.grid, cfg.tile, ws, cfg.heads, out=out, stream=stream)
+    iters = max(args.steps, 10)
+    ms_local = time_launches(local, stream, iters)
+    ms_global = time_launches(glob, stream, iters)
+    ms_fwd = time_launches(step, stream, iters)
+
+    B, n, H, d, W, G = cfg.batch, cfg.n, cfg.heads, cfg.head_dim, cfg.window, cfg.windows
+    rows = B * n * H                                   # (token, head) rows
+    flops_local = 4.0 * d * W * rows                   # QK^T and PV of the local pass
+    flops_global = 4.0 * d * G * rows
+    flops = flops_local + flops_global
+    bytes_per_pass = 8.0 * d * rows                    # read q, k, v (or o1), write o1 (or out): 4 x d x 2 B
+    tokens_per_s = B * n / (ms_per_step * 1e-3)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {
+        "local": {"ms": ms_local, "tflops": flops_local / ms_local / 1e9,
+                  "gbs": bytes_per_pass / ms_local / 1e6},
+        "global": {"ms": ms_global, "tflops": flops_global / ms_global / 1e9,
+                   "gbs": bytes_per_pass / ms_global / 1e6},
+        "forward_events_ms": ms_fwd,
+    }
+    dom = "local" if ms_local >= ms_global else "global"
+    dom_name = {"local": "attn_bf16_kernel<128,4,bf16,fp16> (local pass)",
+                "global": "attn_bf16_kernel<128,4,fp16,bf16> (global pass)"}[dom]
+    achieved = kernels[dom]["gbs"]
+    digest = kernel_source_digest()
+    traffic = traffic_from_profiles(dom, digest)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": dom_name,
+        "algorithmic_bytes_per_launch": bytes_per_pass,
+        "mfma_tflops": round(kernels[dom]["tflops"], 1),
+        "mfma_frac": round(kernels[dom]["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "source_digest": digest,
+    }
+
+    dense = None
+    if not args.no_dense:
+        del out, ws
+        torch.cuda.empty_cache()
+        dense = dense_comparator(sq, inputs, dev)
+
+    base = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
+        base = cpu_baseline(cfg, qc, kc, vc, args.cpu_heads)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: batch {B}, {H} heads, head_dim {d}, grid {'x'.join(map(str, cfg.grid))}, "
+                        f"tile {'x'.join(map(str, cfg.tile))} (W={W}, G={G}), q,k,v iid N(0,1) bf16",
+            "batch": B, "tokens": n, "heads": H, "head_dim": d,
+            "grid": list(cfg.grid), "tile": list(cfg.tile), "parallelism": "none (1 GPU)",
+        },
+        "tflops": round(tflops, 1),
+        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "flops_per_step": flops,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "dense_comparator": dense,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def dense_comparator(sq, inputs, dev):
+    """SQuad forward vs dense full attention on the 5B-DiT-shaped workload."""
+    import torch
+
+    cfg = inputs.CONFIGS["dit5b_bf16"]
+    print("[bench] dense comparator on dit5b_bf16", file=sys.stderr, flush=True)
+    qc, kc, vc = inputs.config_inputs(cfg)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(sq.squad_attn_workspace_size(cfg.grid, cfg.tile, cfg.heads, 1, 128, cfg.dtype),
+                     dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev)
+    fwd = lambda: sq.squad_attn_forward(q, k, v, cfg.grid, cfg.tile, cfg.heads, out=out, workspace=ws, stream=s)
+    dense = lambda: sq.squad_dense_attn_forward(q, k, v, out=out, stream=s)
+    for f in (fwd, dense):
+        f()
+    torch.cuda.synchronize()
+    ms_sq = time_launches(fwd, s, 20)
+    ms_dense = time_launches(dense, s, 5)
+    n, H, d, W, G = cfg.n, cfg.heads, cfg.head_dim, cfg.window, cfg.windows
+    f_sq = 4.0 * d * (W + G) * n * H
+    f_dense = 4.0 * d * n * n * H
+    return {
+        "workload": f"{cfg.name}: grid {'x'.join(map(str, cfg.grid))}, tile {'x'.join(map(str, cfg.tile))}, "
+                    f"{H} heads, head_dim {d}",
+        "squad_ms": round(ms_sq, 4),
+        "dense_ms": round(ms_dense, 4),
+        "latency_ratio": round(ms_dense / ms_sq, 2),
+        "flop_ratio": round(f_dense / f_sq, 2),
+        "dense_tflops": round(f_dense / ms_dense / 1e9, 1),
+        "squad_tflops": round(f_sq / ms_sq / 1e9, 1),
+    }
+
+
+if __name__ == "__main__":
+    main()

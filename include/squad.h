@@ -1,0 +1,190 @@
+/*
+ * squad.h - C ABI of libsquad, the SQuad-Attention forward path for AMD MI355X (gfx950).
+ *
+ * SQuad-Attention replaces full softmax self-attention over the n latent tokens of
+ * a video diffusion transformer by two softmax passes of O(n*sqrt(n)) total cost
+ * (pages titled "SQuad: Sub-Quadratic Attention Distillation for Efficient Video
+ * Generation"; the operator is defined in the gist.science technical summary,
+ * section "Methodologie: SQuad", item "1. SQuad-Attention Operator"):
+ *
+ *   local pass  Attn_L : softmax attention among the tokens of each fixed window;
+ *   global pass Attn_G : softmax attention among the tokens at the same relative
+ *                        position (offset) inside their windows, across all windows;
+ *   composition        : the local output is the value stream of the global pass,
+ *                        out = Attn_G(q, k, Attn_L(q, k, v)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tokens are the cells of a T x H x W latent grid (grid[3] = {T, H, W}), numbered
+ * row-major over (t, h, w); n = T*H*W.  A window is a tt x th x tw tile
+ * (tile[3] = {tt, th, tw}); Wn = tt*th*tw tokens per window, G = n / Wn windows.
+ * Windows are numbered row-major over the window grid (T/tt, H/th, W/tw) and the
+ * offset of a token inside its window row-major over (tt, th, tw).
+ *
+ * Token-order tensors are contiguous [batch, n, heads, head_dim] (= [B, n, hidden]).
+ * Window-major tensors are contiguous [batch, heads, G, Wn, head_dim]; group-major
+ * tensors are contiguous [batch, heads, Wn, G, head_dim].
+ *
+ * dtype: SQUAD_DTYPE_F32 (all tensors fp32, fp32 arithmetic throughout) or
+ * SQUAD_DTYPE_BF16 (bf16 tensors; fp32 accumulation and softmax; the attention
+ * weights are rounded to the value type for the weights-times-values product).
+ * Inside squad_attn_forward the local output is held in fp16 between the two
+ * passes (same bytes as bf16, three more significand bits); values of magnitude
+ * 65504 or more overflow there and surface as inf/nan in the output.
+ * head_dim must be 64 or 128.
+ * scale <= 0 selects the softmax scale 1/sqrt(head_dim).
+ *
+ * Pointers are device pointers that the caller owns; base pointers must be 16-byte
+ * aligned.  The library never allocates or frees device memory and never
+ * synchronises: work is enqueued on `stream` (NULL = the null stream) and kernel
+ * faults surface at the caller's next synchronisation.  Inputs are read-only;
+ * outputs may not overlap inputs or the workspace.  Every argument check runs on
+ * the host before anything is enqueued, so a nonzero status leaves the outputs
+ * untouched.  The library keeps no mutable global state and is reentrant.
+ */
+#ifndef SQUAD_H
+#define SQUAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* squad_stream_t; /* the same type as hipStream_t */
+
+enum squad_status {
+  SQUAD_OK = 0,
+  SQUAD_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, unknown selector          */
+  SQUAD_ERR_SHAPE = 2,       /* grid not a whole number of tiles, sizes too large    */
+  SQUAD_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, or dtype unknown                */
+  SQUAD_ERR_ALIAS = 4,       /* an output overlaps an input or the workspace         */
+  SQUAD_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned                */
+  SQUAD_ERR_WORKSPACE = 6,   /* workspace null or smaller than required             */
+  SQUAD_ERR_HIP = 7          /* a HIP call failed (no device, launch failure)        */
+};
+
+enum squad_dtype { SQUAD_DTYPE_F32 = 0, SQUAD_DTYPE_BF16 = 1 };
+
+/* Static, human-readable text for a status code. */
+const char* squad_status_string(int status);
+
+/*
+ * SQuad-Attention forward (local pass, then global pass with the local output as
+ * its value stream; technical summary, "1. SQuad-Attention Operator").
+ *   q, k, v, out : token order [batch, n, heads, head_dim], dtype `dtype`.
+ *   workspace    : device scratch of at least squad_attn_workspace_size(...) bytes;
+ *                  holds the local output, group-major [batch, heads, Wn, G,
+ *                  head_dim] (fp16 for bf16 calls, fp32 for fp32 calls).
+ * Enqueues two kernels on `stream`: squad_attn_forward_local, then
+ * squad_attn_forward_global.
+ */
+int squad_attn_forward(const void* q, const void* k, const void* v,
+                       const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                       void* out, int32_t batch, int32_t head_dim, int32_t dtype,
+                       float scale, void* workspace, size_t workspace_bytes,
+                       squad_stream_t stream);
+
+/*
+ * First half of squad_attn_forward: the local pass ("1. SQuad-Attention Operator",
+ * Local Pass), writing its output into `workspace` in the layout described above.
+ */
+int squad_attn_forward_local(const void* q, const void* k, const void* v,
+                             const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                             int32_t batch, int32_t head_dim, int32_t dtype, float scale,
+                             void* workspace, size_t workspace_bytes, squad_stream_t stream);
+
+/*
+ * Second half of squad_attn_forward: the global pass ("1. SQuad-Attention
+ * Operator", Global Pass and Compositie) over the local output that
+ * squad_attn_forward_local left in `workspace`, writing `out` in token order.
+ */
+int squad_attn_forward_global(const void* q, const void* k,
+                              const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                              void* out, int32_t batch, int32_t head_dim, int32_t dtype,
+                              float scale, const void* workspace, size_t workspace_bytes,
+                              squad_stream_t stream);
+
+/* Bytes of workspace squad_attn_forward needs (batch*heads*n*head_dim elements of
+ * `dtype`); 0 if the arguments are invalid. */
+size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                                 int32_t batch, int32_t head_dim, int32_t dtype);
+
+/*
+ * Local pass alone (Attn_L): o1 = softmax attention inside each window.
+ * q, k, v, o1 token order [batch, n, heads, head_dim].
+ */
+int squad_local_pass(const void* q, const void* k, const void* v,
+                     const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                     void* o1, int32_t batch, int32_t head_dim, int32_t dtype,
+                     float scale, squad_stream_t stream);
+
+/*
+ * Global pass alone (Attn_G): out = softmax attention among same-offset tokens
+ * across windows, with `vstream` as the value stream (in the operator, the local
+ * output).  All four tensors token order [batch, n, heads, head_dim].
+ */
+int squad_global_pass(const void* q, const void* k, const void* vstream,
+                      const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                      void* out, int32_t batch, int32_t head_dim, int32_t dtype,
+                      float scale, squad_stream_t stream);
+
+/*
+ * Tile gather: token order [batch, n, heads, head_dim] -> window-major
+ * [batch, heads, G, Wn, head_dim] (the tensor reshaping the method is built from;
+ * technical summary, "Belangrijkste Bijdragen").  An exact copy.
+ */
+int squad_tile_gather(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
+                      int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                      squad_stream_t stream);
+
+/* Tile scatter: the inverse of squad_tile_gather (window-major -> token order). */
+int squad_tile_scatter(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
+                       int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                       squad_stream_t stream);
+
+/*
+ * Window-to-group transpose: window-major [batch, heads, G, Wn, head_dim] ->
+ * group-major [batch, heads, Wn, G, head_dim], the regrouping between the local
+ * and the global pass ("1. SQuad-Attention Operator", Global Pass).  Exact copy.
+ */
+int squad_window_to_group(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
+                          int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                          squad_stream_t stream);
+
+/*
+ * Batched short-sequence softmax attention, one independent attention per unit:
+ * q, k, v, out contiguous [units, len, head_dim].  The engine behind both passes.
+ */
+int squad_window_attn(const void* q, const void* k, const void* v, void* out,
+                      int32_t units, int32_t len, int32_t head_dim, int32_t dtype,
+                      float scale, squad_stream_t stream);
+
+/*
+ * Dense full softmax self-attention over all n tokens (the quadratic operator the
+ * method replaces; abstract).  Comparator only.  q, k, v, out token order
+ * [batch, n, heads, head_dim].
+ */
+int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* out,
+                             int32_t batch, int32_t n, int32_t heads, int32_t head_dim,
+                             int32_t dtype, float scale, squad_stream_t stream);
+
+/*
+ * Host-only inspection of the address maps the kernels use (no device needed).
+ * Writes, for every (batch, head, unit, row) in the kernels' enumeration order
+ * [batch][heads][units][rows], the element offset that row occupies in the tensor:
+ *   which = 0: local-pass rows in token order   (units = G windows, rows = Wn offsets)
+ *   which = 1: global-pass rows in token order  (units = Wn offsets, rows = G windows)
+ *   which = 2: local output in the group-major workspace (units = G, rows = Wn)
+ *   which = 3: global-pass value rows in the workspace   (units = Wn, rows = G)
+ * offsets must hold batch*heads*n entries.
+ */
+int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t tile[3],
+                            int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQUAD_H */

@@ -1,0 +1,265 @@
+"""SQuad-Attention forward on AMD MI355X: thin Python binding over libsquad.so.
+
+Every function here only checks and marshals arguments and calls the C ABI of the
+same name (include/squad.h); all arithmetic runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no fallback: if
+the library is missing, calls raise.
+
+Token-order tensors are [batch, n, heads, head_dim] with n = T*H*W tokens of a
+T x H x W latent grid numbered row-major over (t, h, w); a window is a
+tt x th x tw tile of that grid.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "SquadError",
+    "squad_attn_forward",
+    "squad_attn_workspace_size",
+    "squad_attn_forward_local",
+    "squad_attn_forward_global",
+    "squad_local_pass",
+    "squad_global_pass",
+    "squad_tile_gather",
+    "squad_tile_scatter",
+    "squad_window_to_group",
+    "squad_window_attn",
+    "squad_dense_attn_forward",
+    "squad_debug_row_offsets",
+    "DTYPE_CODES",
+]
+
+DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class SquadError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.lib().squad_status_string(status).decode()
+        super().__init__(f"{where}: {_lib.STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(status, where):
+    if status != 0:
+        raise SquadError(status, where)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tensor(x, name, ndim=None, dtype=None, device=None):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {x.device})")
+    if x.dtype not in DTYPE_CODES:
+        raise ValueError(f"{name} must be float32 or bfloat16 (got {x.dtype})")
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError(f"{name} has dtype {x.dtype}, expected {dtype}")
+    if device is not None and x.device != device:
+        raise ValueError(f"{name} is on {x.device}, expected {device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and x.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(x.shape)}")
+    return x
+
+
+def _ptr(x):
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _scale(scale):
+    return ctypes.c_float(0.0 if scale is None else float(scale))
+
+
+def _token_inputs(q, k, v, grid, heads):
+    q = _tensor(q, "q", 4)
+    k = _tensor(k, "k", 4, q.dtype, q.device)
+    v = _tensor(v, "v", 4, q.dtype, q.device)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    B, n, Hh, d = q.shape
+    if heads is not None and int(heads) != Hh:
+        raise ValueError(f"heads={heads} but q has {Hh} heads")
+    T, H, W = (int(x) for x in grid)
+    if T * H * W != n:
+        raise ValueError(f"grid {tuple(grid)} has {T * H * W} tokens, q has {n}")
+    return q, k, v, B, n, Hh, d
+
+
+def _out_like(out, q, name="out"):
+    if out is None:
+        return torch.empty_like(q)
+    out = _tensor(out, name, 4, q.dtype, q.device)
+    if out.shape != q.shape:
+        raise ValueError(f"{name} shape {tuple(out.shape)} != {tuple(q.shape)}")
+    return out
+
+
+def squad_attn_workspace_size(grid, tile, heads, batch, head_dim, dtype):
+    """Bytes of workspace squad_attn_forward needs (0 for invalid arguments)."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.lib().squad_attn_workspace_size(_lib.int3(grid), _lib.int3(tile), int(heads),
+                                                    int(batch), int(head_dim), code))
+
+
+def squad_attn_forward(q, k, v, grid, tile, heads=None, out=None, scale=None, workspace=None,
+                       stream=None):
+    """SQuad-Attention forward: local windowed pass, then the global same-offset pass
+    with the local output as value stream.  Returns out [batch, n, heads, head_dim]."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _out_like(out, q)
+    workspace = _workspace(workspace, squad_attn_workspace_size(grid, tile, Hh, B, d, q.dtype), q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.lib().squad_attn_forward(
+        _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(out), B, d,
+        DTYPE_CODES[q.dtype], _scale(scale), _ptr(workspace), ws_bytes, _stream(stream, q.device))
+    _check(st, "squad_attn_forward")
+    return out
+
+
+def _workspace(workspace, need, device):
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    return workspace
+
+
+def squad_attn_forward_local(q, k, v, grid, tile, heads=None, scale=None, workspace=None, stream=None):
+    """First half of squad_attn_forward: the local pass into the workspace (returned)."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    workspace = _workspace(workspace, squad_attn_workspace_size(grid, tile, Hh, B, d, q.dtype), q.device)
+    st = _lib.lib().squad_attn_forward_local(
+        _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), _lib.int3(tile), Hh, B, d, DTYPE_CODES[q.dtype],
+        _scale(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "squad_attn_forward_local")
+    return workspace
+
+
+def squad_attn_forward_global(q, k, grid, tile, workspace, heads=None, out=None, scale=None, stream=None):
+    """Second half of squad_attn_forward: the global pass over the workspace's local output."""
+    q, k, _, B, n, Hh, d = _token_inputs(q, k, k, grid, heads)
+    out = _out_like(out, q)
+    workspace = _workspace(workspace, 0, q.device)
+    st = _lib.lib().squad_attn_forward_global(
+        _ptr(q), _ptr(k), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(out), B, d, DTYPE_CODES[q.dtype],
+        _scale(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "squad_attn_forward_global")
+    return out
+
+
+def squad_local_pass(q, k, v, grid, tile, heads=None, out=None, scale=None, stream=None):
+    """Local pass alone: softmax attention inside each window (token order in and out)."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _out_like(out, q, "o1")
+    st = _lib.lib().squad_local_pass(_ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), _lib.int3(tile), Hh,
+                                     _ptr(out), B, d, DTYPE_CODES[q.dtype], _scale(scale),
+                                     _stream(stream, q.device))
+    _check(st, "squad_local_pass")
+    return out
+
+
+def squad_global_pass(q, k, vstream, grid, tile, heads=None, out=None, scale=None, stream=None):
+    """Global pass alone: attention among same-offset tokens with `vstream` as values."""
+    q, k, vstream, B, n, Hh, d = _token_inputs(q, k, vstream, grid, heads)
+    out = _out_like(out, q)
+    st = _lib.lib().squad_global_pass(_ptr(q), _ptr(k), _ptr(vstream), _lib.int3(grid), _lib.int3(tile),
+                                      Hh, _ptr(out), B, d, DTYPE_CODES[q.dtype], _scale(scale),
+                                      _stream(stream, q.device))
+    _check(st, "squad_global_pass")
+    return out
+
+
+def _perm(fn_name, src, grid, tile, out_shape, dst, batch, heads, head_dim, stream):
+    src = _tensor(src, "src")
+    if dst is None:
+        dst = torch.empty(out_shape, dtype=src.dtype, device=src.device)
+    else:
+        dst = _tensor(dst, "dst", None, src.dtype, src.device)
+        if tuple(dst.shape) != tuple(out_shape):
+            raise ValueError(f"dst shape {tuple(dst.shape)} != {tuple(out_shape)}")
+    st = getattr(_lib.lib(), fn_name)(_ptr(src), _ptr(dst), _lib.int3(grid), _lib.int3(tile), heads,
+                                      batch, head_dim, DTYPE_CODES[src.dtype], _stream(stream, src.device))
+    _check(st, fn_name)
+    return dst
+
+
+def _geo(grid, tile):
+    T, H, W = (int(x) for x in grid)
+    tt, th, tw = (int(x) for x in tile)
+    if min(tt, th, tw) <= 0 or T % tt or H % th or W % tw:
+        return T * H * W, 0, 0
+    Wn = tt * th * tw
+    return T * H * W, (T * H * W) // Wn, Wn
+
+
+def squad_tile_gather(src, grid, tile, dst=None, stream=None):
+    """Token order [B, n, Hh, d] -> window-major [B, Hh, G, Wn, d] (exact copy)."""
+    B, n, Hh, d = src.shape
+    _, G, Wn = _geo(grid, tile)
+    return _perm("squad_tile_gather", src, grid, tile, (B, Hh, G, Wn, d), dst, B, Hh, d, stream)
+
+
+def squad_tile_scatter(src, grid, tile, dst=None, stream=None):
+    """Window-major [B, Hh, G, Wn, d] -> token order [B, n, Hh, d] (exact copy)."""
+    B, Hh, G, Wn, d = src.shape
+    n, _, _ = _geo(grid, tile)
+    return _perm("squad_tile_scatter", src, grid, tile, (B, n, Hh, d), dst, B, Hh, d, stream)
+
+
+def squad_window_to_group(src, grid, tile, dst=None, stream=None):
+    """Window-major [B, Hh, G, Wn, d] -> group-major [B, Hh, Wn, G, d] (exact copy)."""
+    B, Hh, G, Wn, d = src.shape
+    return _perm("squad_window_to_group", src, grid, tile, (B, Hh, Wn, G, d), dst, B, Hh, d, stream)
+
+
+def squad_window_attn(q, k, v, out=None, scale=None, stream=None):
+    """Independent softmax attention per unit: q, k, v [units, len, head_dim]."""
+    q = _tensor(q, "q", 3)
+    k = _tensor(k, "k", 3, q.dtype, q.device)
+    v = _tensor(v, "v", 3, q.dtype, q.device)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v shapes differ")
+    out = torch.empty_like(q) if out is None else _tensor(out, "out", 3, q.dtype, q.device)
+    U, L, d = q.shape
+    st = _lib.lib().squad_window_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), U, L, d, DTYPE_CODES[q.dtype],
+                                      _scale(scale), _stream(stream, q.device))
+    _check(st, "squad_window_attn")
+    return out
+
+
+def squad_dense_attn_forward(q, k, v, out=None, scale=None, stream=None):
+    """Dense full softmax self-attention over all n tokens: [B, n, Hh, d] (comparator)."""
+    q = _tensor(q, "q", 4)
+    k = _tensor(k, "k", 4, q.dtype, q.device)
+    v = _tensor(v, "v", 4, q.dtype, q.device)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v shapes differ")
+    out = _out_like(out, q)
+    B, n, Hh, d = q.shape
+    st = _lib.lib().squad_dense_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, n, Hh, d,
+                                             DTYPE_CODES[q.dtype], _scale(scale), _stream(stream, q.device))
+    _check(st, "squad_dense_attn_forward")
+    return out
+
+
+def squad_debug_row_offsets(which, grid, tile, heads, batch, head_dim):
+    """Host-side element offsets the kernels use (see include/squad.h); numpy int64."""
+    import numpy as np
+
+    n = int(grid[0]) * int(grid[1]) * int(grid[2])
+    out = np.zeros(int(batch) * int(heads) * n, dtype=np.int64)
+    st = _lib.lib().squad_debug_row_offsets(int(which), _lib.int3(grid), _lib.int3(tile), int(heads),
+                                            int(batch), int(head_dim),
+                                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    _check(st, "squad_debug_row_offsets")
+    return out

@@ -1,0 +1,436 @@
+// squad_api.hip - the C ABI of libsquad: argument checks, address-map set-up and
+// kernel enqueues.  Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "squad.h"
+#include "squad_kernels.h"
+
+using namespace squad;
+
+namespace {
+
+struct Geo {
+  int64_t T, H, W, tt, th, tw;  // grid and tile
+  int64_t nt, nh, nw;           // window grid
+  int64_t G, Wn, n;             // windows, tokens per window, tokens
+};
+
+int make_geo(const int32_t grid[3], const int32_t tile[3], Geo& g) {
+  if (!grid || !tile) return SQUAD_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (grid[i] <= 0 || tile[i] <= 0) return SQUAD_ERR_INVALID_ARG;
+  g.T = grid[0]; g.H = grid[1]; g.W = grid[2];
+  g.tt = tile[0]; g.th = tile[1]; g.tw = tile[2];
+  if (g.T % g.tt || g.H % g.th || g.W % g.tw) return SQUAD_ERR_SHAPE;
+  g.nt = g.T / g.tt; g.nh = g.H / g.th; g.nw = g.W / g.tw;
+  g.n = g.T * g.H * g.W;
+  g.Wn = g.tt * g.th * g.tw;
+  g.G = g.nt * g.nh * g.nw;
+  if (g.n >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  return SQUAD_OK;
+}
+
+int check_common(int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
+  if (heads <= 0 || batch <= 0 || head_dim <= 0) return SQUAD_ERR_INVALID_ARG;
+  if (dtype != SQUAD_DTYPE_F32 && dtype != SQUAD_DTYPE_BF16) return SQUAD_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return SQUAD_ERR_UNSUPPORTED;
+  return SQUAD_OK;
+}
+
+size_t elem_bytes(int32_t dtype) { return dtype == SQUAD_DTYPE_F32 ? 4 : 2; }
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+Mix mix(uint32_t x1, uint32_t x0, int64_t s2, int64_t s1, int64_t s0) {
+  Mix m;
+  m.x1 = FastDiv(x1);
+  m.x0 = FastDiv(x0);
+  m.s2 = s2; m.s1 = s1; m.s0 = s0;
+  return m;
+}
+
+Mix linear(int64_t stride) { return mix(1, 1, stride, 0, 0); }
+
+// Token order [B, n, heads, d]: the window part and the offset part of a token index.
+Mix window_part(const Geo& g, int64_t ts) {
+  return mix((uint32_t)g.nh, (uint32_t)g.nw, g.tt * g.H * g.W * ts, g.th * g.W * ts, g.tw * ts);
+}
+Mix offset_part(const Geo& g, int64_t ts) {
+  return mix((uint32_t)g.th, (uint32_t)g.tw, g.H * g.W * ts, g.W * ts, ts);
+}
+
+RowMap token_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
+  RowMap m;
+  const int64_t ts = heads * d;
+  m.sB = g.n * ts;
+  m.sH = d;
+  m.unit = by_window ? window_part(g, ts) : offset_part(g, ts);
+  m.row = by_window ? offset_part(g, ts) : window_part(g, ts);
+  return m;
+}
+
+// Group-major [B, heads, Wn, G, d] (by_window: units are windows, rows offsets).
+RowMap group_major_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
+  RowMap m;
+  m.sB = heads * g.Wn * g.G * d;
+  m.sH = g.Wn * g.G * d;
+  m.unit = by_window ? linear(d) : linear(g.G * d);
+  m.row = by_window ? linear(g.G * d) : linear(d);
+  return m;
+}
+
+// Window-major [B, heads, G, Wn, d].
+RowMap window_major_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
+  RowMap m;
+  m.sB = heads * g.G * g.Wn * d;
+  m.sH = g.G * g.Wn * d;
+  m.unit = by_window ? linear(g.Wn * d) : linear(d);
+  m.row = by_window ? linear(d) : linear(g.Wn * d);
+  return m;
+}
+
+AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, uint32_t L, uint32_t U,
+                   uint32_t heads, uint32_t batch, int32_t head_dim, float scale) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  a.L = L; a.U = U; a.heads = heads; a.BH = heads * batch;
+  a.fBH = FastDiv(a.BH);
+  a.fHeads = FastDiv(heads);
+  a.units = a.BH * U;
+  const double s = scale > 0.f ? (double)scale : 1.0 / sqrt((double)head_dim);
+  a.c = (float)(s * 1.4426950408889634);  // log2(e)
+  return a;
+}
+
+int run_attn(AttnArgs a, int32_t head_dim, int32_t dtype, hipStream_t stream,
+             VType vtype = VType::kBf16ToBf16) {
+  if (a.units == 0 || a.L == 0) return SQUAD_OK;
+  const hipError_t e = dtype == SQUAD_DTYPE_BF16 ? launch_attn_bf16(a, head_dim, vtype, stream)
+                                                 : launch_attn_f32(a, head_dim, stream);
+  return e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+}
+
+bool too_many_units(uint64_t bh, uint64_t units_per_bh, uint64_t rows) {
+  return bh * units_per_bh >= (uint64_t(1) << 32) || rows >= (uint64_t(1) << 32);
+}
+
+// Shared checks of the grid/tile entry points: geometry, dtype, sizes, pointers.
+int check_grid_call(const int32_t grid[3], const int32_t tile[3], int32_t heads, int32_t batch,
+                    int32_t head_dim, int32_t dtype, Geo& g, size_t& bytes) {
+  int st = make_geo(grid, tile, g);
+  if (st) return st;
+  st = check_common(heads, batch, head_dim, dtype);
+  if (st) return st;
+  const uint64_t bh = (uint64_t)heads * (uint64_t)batch;
+  if (too_many_units(bh, (uint64_t)(g.G > g.Wn ? g.G : g.Wn), bh * (uint64_t)g.n)) return SQUAD_ERR_SHAPE;
+  bytes = (size_t)bh * (size_t)g.n * (size_t)head_dim * elem_bytes(dtype);
+  return SQUAD_OK;
+}
+
+int check_ptrs(const void* const* in, int nin, const void* out, size_t bytes) {
+  for (int i = 0; i < nin; ++i)
+    if (!in[i]) return SQUAD_ERR_INVALID_ARG;
+  if (!out) return SQUAD_ERR_INVALID_ARG;
+  for (int i = 0; i < nin; ++i)
+    if (misaligned(in[i])) return SQUAD_ERR_ALIGN;
+  if (misaligned(out)) return SQUAD_ERR_ALIGN;
+  for (int i = 0; i < nin; ++i)
+    if (overlap(in[i], bytes, out, bytes)) return SQUAD_ERR_ALIAS;
+  return SQUAD_OK;
+}
+
+int run_copy(const void* src, void* dst, const RowMap& ms, const RowMap& md, uint32_t L, uint32_t U,
+             uint32_t heads, uint32_t batch, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  CopyArgs c;
+  memset(&c, 0, sizeof(c));
+  c.src = src; c.dst = dst; c.ms = ms; c.md = md;
+  c.L = L; c.U = U; c.heads = heads; c.BH = heads * batch;
+  c.fL = FastDiv(L); c.fU = FastDiv(U); c.fHeads = FastDiv(heads);
+  c.rows = c.BH * U * L;
+  c.elem_bytes = (uint32_t)elem_bytes(dtype);
+  const uint32_t chunks = (uint32_t)(head_dim * c.elem_bytes / 16);
+  c.row_chunks_log2 = 0;
+  while ((1u << c.row_chunks_log2) < chunks) ++c.row_chunks_log2;
+  if (((uint64_t)c.rows << c.row_chunks_log2) >= (uint64_t(1) << 40)) return SQUAD_ERR_SHAPE;
+  return launch_row_copy(c, stream) == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* squad_status_string(int status) {
+  switch (status) {
+    case SQUAD_OK: return "ok";
+    case SQUAD_ERR_INVALID_ARG: return "invalid argument (null pointer, size <= 0 or unknown selector)";
+    case SQUAD_ERR_SHAPE: return "shape error (grid not a whole number of tiles, or sizes too large)";
+    case SQUAD_ERR_UNSUPPORTED: return "unsupported (head_dim must be 64 or 128; dtype 0 = fp32, 1 = bf16)";
+    case SQUAD_ERR_ALIAS: return "an output overlaps an input or the workspace";
+    case SQUAD_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case SQUAD_ERR_WORKSPACE: return "workspace null or smaller than squad_attn_workspace_size()";
+    case SQUAD_ERR_HIP: return "HIP error (no device, or a launch failed)";
+    default: return "unknown status";
+  }
+}
+
+size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                                 int32_t batch, int32_t head_dim, int32_t dtype) {
+  Geo g;
+  size_t bytes = 0;
+  if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes)) return 0;
+  return bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by squad_attn_forward and its two halves: `in` holds the nin input
+// pointers, `out` is null for the local half (whose only output is the workspace).
+int check_forward(const void* const* in, int nin, const void* out, const int32_t grid[3],
+                  const int32_t tile[3], int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                  float scale, const void* workspace, size_t workspace_bytes, Geo& g) {
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  if (st) return st;
+  for (int i = 0; i < nin; ++i)
+    if (!in[i]) return SQUAD_ERR_INVALID_ARG;
+  if (out) {
+    st = check_ptrs(in, nin, out, bytes);
+    if (st) return st;
+  } else {
+    for (int i = 0; i < nin; ++i)
+      if (misaligned(in[i])) return SQUAD_ERR_ALIGN;
+  }
+  if (!workspace || workspace_bytes < bytes) return SQUAD_ERR_WORKSPACE;
+  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
+  for (int i = 0; i < nin; ++i)
+    if (overlap(in[i], bytes, workspace, bytes)) return SQUAD_ERR_ALIAS;
+  if (out && overlap(out, bytes, workspace, bytes)) return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  return SQUAD_OK;
+}
+
+// Local pass of the forward: units = windows, rows = offsets; the output goes to the
+// workspace, group-major.  bf16: held as fp16 between the passes (its bf16 rounding
+// would take about half of the 1.5e-2 error budget; fp16 costs the same bytes).
+int forward_local(const void* q, const void* k, const void* v, const Geo& g, int32_t heads, int32_t batch,
+                  int32_t head_dim, int32_t dtype, float scale, void* workspace, hipStream_t s) {
+  AttnArgs a = attn_args(q, k, v, workspace, (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, scale);
+  a.mqk = token_map(g, heads, head_dim, true);
+  a.mv = a.mqk;
+  a.mo = group_major_map(g, heads, head_dim, true);
+  return run_attn(a, head_dim, dtype, s, VType::kBf16ToF16);
+}
+
+// Global pass of the forward: units = offset groups, rows = windows; the value
+// stream is the local output in the workspace; the output goes to token order.
+int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_t heads, int32_t batch,
+                   int32_t head_dim, int32_t dtype, float scale, const void* workspace, hipStream_t s) {
+  AttnArgs a = attn_args(q, k, workspace, out, (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, scale);
+  a.mqk = token_map(g, heads, head_dim, false);
+  a.mv = group_major_map(g, heads, head_dim, false);
+  a.mo = a.mqk;
+  return run_attn(a, head_dim, dtype, s, VType::kF16ToBf16);
+}
+
+}  // namespace
+
+extern "C" {
+
+int squad_attn_forward(const void* q, const void* k, const void* v, const int32_t grid[3],
+                       const int32_t tile[3], int32_t heads, void* out, int32_t batch,
+                       int32_t head_dim, int32_t dtype, float scale, void* workspace,
+                       size_t workspace_bytes, squad_stream_t stream) {
+  Geo g;
+  if (!out) return SQUAD_ERR_INVALID_ARG;
+  const void* in[3] = {q, k, v};
+  int st = check_forward(in, 3, out, grid, tile, heads, batch, head_dim, dtype, scale, workspace,
+                         workspace_bytes, g);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = forward_local(q, k, v, g, heads, batch, head_dim, dtype, scale, workspace, s);
+  if (st) return st;
+  return forward_global(q, k, out, g, heads, batch, head_dim, dtype, scale, workspace, s);
+}
+
+int squad_attn_forward_local(const void* q, const void* k, const void* v, const int32_t grid[3],
+                             const int32_t tile[3], int32_t heads, int32_t batch, int32_t head_dim,
+                             int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                             squad_stream_t stream) {
+  Geo g;
+  const void* in[3] = {q, k, v};
+  int st = check_forward(in, 3, nullptr, grid, tile, heads, batch, head_dim, dtype, scale, workspace,
+                         workspace_bytes, g);
+  if (st) return st;
+  return forward_local(q, k, v, g, heads, batch, head_dim, dtype, scale, workspace, (hipStream_t)stream);
+}
+
+int squad_attn_forward_global(const void* q, const void* k, const int32_t grid[3], const int32_t tile[3],
+                              int32_t heads, void* out, int32_t batch, int32_t head_dim, int32_t dtype,
+                              float scale, const void* workspace, size_t workspace_bytes,
+                              squad_stream_t stream) {
+  Geo g;
+  if (!out) return SQUAD_ERR_INVALID_ARG;
+  const void* in[2] = {q, k};
+  int st = check_forward(in, 2, out, grid, tile, heads, batch, head_dim, dtype, scale, workspace,
+                         workspace_bytes, g);
+  if (st) return st;
+  return forward_global(q, k, out, g, heads, batch, head_dim, dtype, scale, workspace, (hipStream_t)stream);
+}
+
+int squad_local_pass(const void* q, const void* k, const void* v, const int32_t grid[3],
+                     const int32_t tile[3], int32_t heads, void* o1, int32_t batch,
+                     int32_t head_dim, int32_t dtype, float scale, squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  if (st) return st;
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, o1, bytes);
+  if (st) return st;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  AttnArgs a = attn_args(q, k, v, o1, (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, scale);
+  a.mqk = token_map(g, heads, head_dim, true);
+  a.mv = a.mqk;
+  a.mo = a.mqk;
+  return run_attn(a, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_global_pass(const void* q, const void* k, const void* vstream, const int32_t grid[3],
+                      const int32_t tile[3], int32_t heads, void* out, int32_t batch,
+                      int32_t head_dim, int32_t dtype, float scale, squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  if (st) return st;
+  const void* in[3] = {q, k, vstream};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  AttnArgs a = attn_args(q, k, vstream, out, (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, scale);
+  a.mqk = token_map(g, heads, head_dim, false);
+  a.mv = a.mqk;
+  a.mo = a.mqk;
+  return run_attn(a, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_tile_gather(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
+                      int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                      squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  if (st) return st;
+  const void* in[1] = {src};
+  st = check_ptrs(in, 1, dst, bytes);
+  if (st) return st;
+  return run_copy(src, dst, token_map(g, heads, head_dim, true), window_major_map(g, heads, head_dim, true),
+                  (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_tile_scatter(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
+                       int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                       squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  if (st) return st;
+  const void* in[1] = {src};
+  st = check_ptrs(in, 1, dst, bytes);
+  if (st) return st;
+  return run_copy(src, dst, window_major_map(g, heads, head_dim, true), token_map(g, heads, head_dim, true),
+                  (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_window_to_group(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
+                          int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
+                          squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  if (st) return st;
+  const void* in[1] = {src};
+  st = check_ptrs(in, 1, dst, bytes);
+  if (st) return st;
+  // enumerate rows in the group-major (destination) order: units = offsets, rows = windows
+  return run_copy(src, dst, window_major_map(g, heads, head_dim, false), group_major_map(g, heads, head_dim, false),
+                  (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_window_attn(const void* q, const void* k, const void* v, void* out, int32_t units,
+                      int32_t len, int32_t head_dim, int32_t dtype, float scale,
+                      squad_stream_t stream) {
+  if (units <= 0 || len <= 0) return SQUAD_ERR_INVALID_ARG;
+  int st = check_common(1, 1, head_dim, dtype);
+  if (st) return st;
+  const size_t bytes = (size_t)units * (size_t)len * (size_t)head_dim * elem_bytes(dtype);
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  AttnArgs a = attn_args(q, k, v, out, (uint32_t)len, (uint32_t)units, 1, 1, head_dim, scale);
+  RowMap m;
+  m.sB = 0; m.sH = 0;
+  m.unit = linear((int64_t)len * head_dim);
+  m.row = linear(head_dim);
+  a.mqk = m; a.mv = m; a.mo = m;
+  return run_attn(a, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                             int32_t n, int32_t heads, int32_t head_dim, int32_t dtype, float scale,
+                             squad_stream_t stream) {
+  if (n <= 0) return SQUAD_ERR_INVALID_ARG;
+  int st = check_common(heads, batch, head_dim, dtype);
+  if (st) return st;
+  if ((uint64_t)batch * (uint64_t)heads >= (uint64_t(1) << 32)) return SQUAD_ERR_SHAPE;
+  const size_t bytes = (size_t)batch * (size_t)n * (size_t)heads * (size_t)head_dim * elem_bytes(dtype);
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  AttnArgs a = attn_args(q, k, v, out, (uint32_t)n, 1, heads, batch, head_dim, scale);
+  RowMap m;
+  m.sB = (int64_t)n * heads * head_dim;
+  m.sH = head_dim;
+  m.unit = linear(0);
+  m.row = linear((int64_t)heads * head_dim);
+  a.mqk = m; a.mv = m; a.mo = m;
+  return run_attn(a, head_dim, dtype, (hipStream_t)stream);
+}
+
+int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                            int32_t batch, int32_t head_dim, int64_t* offsets) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, SQUAD_DTYPE_BF16, g, bytes);
+  if (st) return st;
+  if (!offsets) return SQUAD_ERR_INVALID_ARG;
+  RowMap m;
+  uint32_t U, L;
+  switch (which) {
+    case 0: m = token_map(g, heads, head_dim, true); U = (uint32_t)g.G; L = (uint32_t)g.Wn; break;
+    case 1: m = token_map(g, heads, head_dim, false); U = (uint32_t)g.Wn; L = (uint32_t)g.G; break;
+    case 2: m = group_major_map(g, heads, head_dim, true); U = (uint32_t)g.G; L = (uint32_t)g.Wn; break;
+    case 3: m = group_major_map(g, heads, head_dim, false); U = (uint32_t)g.Wn; L = (uint32_t)g.G; break;
+    default: return SQUAD_ERR_INVALID_ARG;
+  }
+  size_t i = 0;
+  for (uint32_t b = 0; b < (uint32_t)batch; ++b)
+    for (uint32_t h = 0; h < (uint32_t)heads; ++h)
+      for (uint32_t s = 0; s < U; ++s) {
+        const int64_t base = m.base(b, h, s);
+        for (uint32_t r = 0; r < L; ++r) offsets[i++] = base + m.row_off(r);
+      }
+  return SQUAD_OK;
+}
+
+}  // extern "C"

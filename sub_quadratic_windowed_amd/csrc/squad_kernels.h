@@ -1,0 +1,56 @@
+// squad_kernels.h - launch interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "squad_map.h"
+
+namespace squad {
+
+// One launch runs `units` independent softmax attentions of L rows each: for unit u
+// and query row i, out_i = sum_j softmax_j(scale * <q_i, k_j>) v_j over the unit's L
+// rows.  Units are numbered u = s * BH + bh (s = unit within a (batch, head) pair,
+// bh = batch * heads + head), so neighbouring units are the heads of one window or
+// group.  Rows of q and k are located with mqk, rows of v with mv, output rows
+// with mo.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  RowMap mqk, mv, mo;
+  uint32_t L;        // rows (queries = keys) per unit
+  uint32_t U;        // units per (batch, head)
+  uint32_t heads;    // heads per batch element
+  uint32_t BH;       // batch * heads
+  FastDiv fBH, fHeads;
+  uint32_t units;    // BH * U
+  uint32_t nchunks;  // query chunks per unit (set by the launcher)
+  float c;           // softmax scale * log2(e)
+};
+
+// Value and output types of the bf16 engine (q and k are always bf16).  The local
+// pass of squad_attn_forward writes its output as fp16 (three more significand bits
+// than bf16, same bytes) and the global pass reads it back as fp16 values.
+enum class VType { kBf16ToBf16, kBf16ToF16, kF16ToBf16 };
+
+hipError_t launch_attn_bf16(AttnArgs a, int head_dim, VType vtype, hipStream_t stream);
+hipError_t launch_attn_f32(AttnArgs a, int head_dim, hipStream_t stream);
+
+// Row-permutation copy: rows e = (bh * U + s) * L + r for bh < BH, s < U, r < L;
+// row e is read at src + ms(b, h, s, r) and written at dst + md(b, h, s, r).
+struct CopyArgs {
+  const void* src;
+  void* dst;
+  RowMap ms, md;      // offsets in elements
+  uint32_t L, U, heads, BH;
+  FastDiv fL, fU, fHeads;
+  uint32_t rows;      // BH * U * L
+  uint32_t row_chunks_log2;  // log2 of the 16-byte chunks per row
+  uint32_t elem_bytes;  // 2 or 4
+};
+
+hipError_t launch_row_copy(CopyArgs a, hipStream_t stream);
+
+}  // namespace squad

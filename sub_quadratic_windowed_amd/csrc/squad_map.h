@@ -1,0 +1,75 @@
+// squad_map.h - address maps from (batch, head, unit, row) to tensor element offsets.
+//
+// Both passes of SQuad-Attention run one softmax attention per "unit": a window
+// (local pass) or an offset group (global pass).  A unit's rows are its tokens.
+// The maps below turn (b, h, unit s, row r) into the element offset of that row in
+// a tensor, so the attention kernels read token-order inputs and write their
+// outputs in place, with the window gather, the window-to-group regroup and the
+// final scatter folded into their loads and stores.
+//
+// Every map has the form
+//     off = b*sB + h*sH + mix(s; U1, U0; A2, A1, A0) + mix(r; R1, R0; C2, C1, C0)
+// where mix(x; X1, X0; S2, S1, S0) splits x into mixed-radix digits
+// (x2, x1, x0) with x0 = x % X0, x1 = (x / X0) % X1, x2 = x / (X0*X1) and returns
+// x2*S2 + x1*S1 + x0*S0.  A token (t, h, w) of a T x H x W grid lies at token index
+// (t*H + h)*W + w; with tile (tt, th, tw) and window grid (nt, nh, nw) =
+// (T/tt, H/th, W/tw), window g = (gt*nh + gh)*nw + gw and offset
+// p = (at*th + ah)*tw + aw sit at t = gt*tt + at, h = gh*th + ah, w = gw*tw + aw,
+// so the token index splits into a window part and an offset part, each a
+// mixed-radix mix of its digits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace squad {
+
+// Division by a runtime constant d >= 1 for dividends x < 2^32:
+// q = floor(x * M / 2^64) with M = ceil(2^64 / d) is exact because the error term
+// x * (M*d - 2^64) / (d * 2^64) < x / 2^64 < 1/d (Granlund & Montgomery, 1994).
+struct FastDiv {
+  uint64_t mul;   // ceil(2^64 / d); unused for d == 1
+  uint32_t d;
+
+  __host__ __device__ FastDiv() : mul(0), d(1) {}
+  __host__ explicit FastDiv(uint32_t divisor) : mul(0), d(divisor) {
+    if (d > 1) {
+      unsigned __int128 one = 1;
+      mul = (uint64_t)(((one << 64) + d - 1) / d);
+    }
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t x) const {
+    if (d == 1) return x;
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)__umul64hi((uint64_t)x, mul);
+#else
+    return (uint32_t)(((unsigned __int128)x * mul) >> 64);
+#endif
+  }
+};
+
+struct Mix {
+  FastDiv x1, x0;     // radices X1, X0
+  int64_t s2, s1, s0; // strides of the digits (elements)
+
+  __host__ __device__ __forceinline__ int64_t at(uint32_t x) const {
+    uint32_t q0 = x0.div(x);
+    uint32_t d0 = x - q0 * x0.d;
+    uint32_t q1 = x1.div(q0);
+    uint32_t d1 = q0 - q1 * x1.d;
+    return (int64_t)q1 * s2 + (int64_t)d1 * s1 + (int64_t)d0 * s0;
+  }
+};
+
+struct RowMap {
+  int64_t sB, sH; // batch and head strides (elements)
+  Mix unit;       // unit index -> offset
+  Mix row;        // row index  -> offset
+
+  __host__ __device__ __forceinline__ int64_t base(uint32_t b, uint32_t h, uint32_t s) const {
+    return (int64_t)b * sB + (int64_t)h * sH + unit.at(s);
+  }
+  __host__ __device__ __forceinline__ int64_t row_off(uint32_t r) const { return row.at(r); }
+};
+
+}  // namespace squad

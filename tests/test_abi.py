@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/squad.h
+declares, rejects bad arguments before touching the device, and its address maps
+are the oracle's window partition.  No GPU needed."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from sub_quadratic_windowed_amd import _lib
+import sub_quadratic_windowed_amd as sq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "squad.h")
+
+OK, INVALID, SHAPE, UNSUP, ALIAS, ALIGN, WORKSPACE, HIP = range(8)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(squad_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.lib()
+    declared = header_functions()
+    assert len(declared) >= 10, declared
+    assert sorted(_lib.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    for s in range(8):
+        assert lib.squad_status_string(s).decode()
+    assert lib.squad_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_size():
+    assert sq.squad_attn_workspace_size((64, 48, 80), (4, 12, 10), 24, 1, 128, 1) == 245760 * 24 * 128 * 2
+    assert sq.squad_attn_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 64, 0) == 256 * 2 * 64 * 4
+    assert sq.squad_attn_workspace_size((4, 8, 8), (3, 4, 4), 2, 1, 64, 0) == 0
+    assert sq.squad_attn_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 96, 1) == 0
+
+
+# fake, never-dereferenced device addresses: argument checks must fire first
+A = 0x10000000
+B = 0x20000000
+C = 0x30000000
+O = 0x40000000
+WS = 0x50000000
+
+
+def fwd(q=A, k=B, v=C, grid=(4, 8, 8), tile=(1, 4, 4), heads=2, out=O, batch=1, d=64, dtype=1,
+        scale=0.0, ws=WS, ws_bytes=1 << 30):
+    return _lib.lib().squad_attn_forward(
+        ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), _lib.int3(grid), _lib.int3(tile), heads,
+        ctypes.c_void_p(out), batch, d, dtype, ctypes.c_float(scale), ctypes.c_void_p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(out=0), INVALID), (dict(heads=0), INVALID), (dict(batch=-1), INVALID),
+    (dict(grid=(4, 0, 8)), INVALID), (dict(tile=(1, 4, -4)), INVALID),
+    (dict(tile=(3, 4, 4)), SHAPE), (dict(tile=(1, 5, 4)), SHAPE), (dict(grid=(1 << 11, 1 << 11, 1 << 10)), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(dtype=2), UNSUP),
+    (dict(q=A + 8), ALIGN), (dict(out=O + 4), ALIGN), (dict(ws=WS + 2), ALIGN),
+    (dict(out=A), ALIAS), (dict(out=B + 64), ALIAS), (dict(ws=C), ALIAS), (dict(ws=O), ALIAS),
+    (dict(ws=0), WORKSPACE), (dict(ws_bytes=256 * 2 * 64 * 2 - 1), WORKSPACE),
+    (dict(scale=float("nan")), INVALID),
+])
+def test_forward_rejects_bad_arguments(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = _lib.lib()
+    p = ctypes.c_void_p
+    g, t = _lib.int3((4, 8, 8)), _lib.int3((1, 4, 4))
+    for fn in (lib.squad_tile_gather, lib.squad_tile_scatter, lib.squad_window_to_group):
+        assert fn(p(A), p(0), g, t, 2, 1, 64, 1, None) == INVALID
+        assert fn(p(A), p(A), g, t, 2, 1, 64, 1, None) == ALIAS
+        assert fn(p(A), p(B), g, _lib.int3((1, 3, 4)), 2, 1, 64, 1, None) == SHAPE
+        assert fn(p(A), p(B + 2), g, t, 2, 1, 64, 1, None) == ALIGN
+    for fn in (lib.squad_local_pass, lib.squad_global_pass):
+        assert fn(p(A), p(B), p(C), g, t, 2, p(C), 1, 64, 1, ctypes.c_float(0), None) == ALIAS
+        assert fn(p(A), p(B), p(C), g, t, 2, p(O), 1, 32, 1, ctypes.c_float(0), None) == UNSUP
+    assert lib.squad_window_attn(p(A), p(B), p(C), p(O), 0, 16, 64, 1, ctypes.c_float(0), None) == INVALID
+    assert lib.squad_window_attn(p(A), p(B), p(C), p(A), 4, 16, 64, 1, ctypes.c_float(0), None) == ALIAS
+    assert lib.squad_dense_attn_forward(p(A), p(B), p(C), p(O), 1, 0, 2, 64, 1, ctypes.c_float(0), None) == INVALID
+    assert lib.squad_dense_attn_forward(p(A), p(B), p(C), p(O), 1, 256, 2, 64, 7, ctypes.c_float(0), None) == UNSUP
+    off = np.zeros(512, np.int64)
+    ptr = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    assert lib.squad_debug_row_offsets(4, g, t, 2, 1, 64, ptr) == INVALID
+
+
+# ---------------------------------------------------------------- address maps vs the oracle's partition
+
+MAP_SHAPES = [((4, 8, 8), (1, 4, 4)), ((2, 4, 6), (2, 2, 3)), ((3, 2, 4), (1, 2, 2)), ((2, 3, 4), (1, 1, 1)),
+              ((1, 4, 4), (1, 4, 4)), ((32, 24, 40), (2, 8, 10)), ((4, 6, 10), (4, 6, 10))]
+
+
+@pytest.mark.parametrize("grid,tile", MAP_SHAPES)
+@pytest.mark.parametrize("batch,heads,d", [(1, 2, 64), (2, 3, 128)])
+def test_row_maps_are_the_window_partition(grid, tile, batch, heads, d):
+    idx = oracle.window_index(grid, tile)                 # [G, Wn] token of (window, offset)
+    G, Wn = idx.shape
+    n = G * Wn
+    b = np.arange(batch)[:, None, None, None]
+    h = np.arange(heads)[None, :, None, None]
+    # which = 0: (b, h, g, p) -> token order offset of token idx[g, p]
+    want0 = ((b * n + idx[None, None]) * heads + h) * d
+    got0 = sq.squad_debug_row_offsets(0, grid, tile, heads, batch, d).reshape(batch, heads, G, Wn)
+    assert np.array_equal(got0, want0)
+    # which = 1: (b, h, p, g) -> token idx[g, p]
+    want1 = ((b * n + idx.T[None, None]) * heads + h) * d
+    got1 = sq.squad_debug_row_offsets(1, grid, tile, heads, batch, d).reshape(batch, heads, Wn, G)
+    assert np.array_equal(got1, want1)
+    # which = 2 / 3: group-major [B, heads, Wn, G, d]
+    gi = np.arange(G)[:, None]
+    pi = np.arange(Wn)[None, :]
+    want2 = (((b * heads + h) * Wn + pi[None, None]) * G + gi[None, None]) * d
+    got2 = sq.squad_debug_row_offsets(2, grid, tile, heads, batch, d).reshape(batch, heads, G, Wn)
+    assert np.array_equal(got2, want2)
+    got3 = sq.squad_debug_row_offsets(3, grid, tile, heads, batch, d).reshape(batch, heads, Wn, G)
+    assert np.array_equal(got3, np.swapaxes(want2, 2, 3))
+    # every map is a bijection onto the rows of its tensor
+    for got in (got0, got1, got2, got3):
+        assert np.array_equal(np.sort(got.ravel()), np.arange(batch * heads * n) * d)
+
+
+def test_row_maps_at_full_size():
+    """The largest configuration: both token maps cover every row exactly once."""
+    grid, tile, heads = (64, 48, 80), (4, 12, 10), 24
+    n = 64 * 48 * 80
+    for which in (0, 1):
+        got = sq.squad_debug_row_offsets(which, grid, tile, heads, 1, 128)
+        assert got.size == n * heads
+        assert np.array_equal(np.sort(got), np.arange(n * heads) * 128)
+    idx = oracle.window_index(grid, tile)
+    got0 = sq.squad_debug_row_offsets(0, grid, tile, heads, 1, 128).reshape(heads, *idx.shape)
+    assert np.array_equal(got0[5], (idx * heads + 5) * 128)
+
+
+def _device_count():
+    try:
+        import torch
+        return torch.cuda.device_count()
+    except Exception:  # pragma: no cover
+        return 0
+
+
+@pytest.mark.skipif(_device_count() > 0, reason="fake pointers must never reach a real device")
+def test_valid_call_without_device_reports_hip_error():
+    assert fwd() == HIP

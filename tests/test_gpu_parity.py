@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances are max-abs: 1e-4 for fp32 inputs, 1.5e-2 for bf16 inputs with fp32
+accumulation.  The oracle is always fed the exact values the GPU saw (bf16 inputs
+upcast exactly).  Integer and byte work (the permutations) must be bit-exact.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sub_quadratic_windowed_amd import inputs
+import sub_quadratic_windowed_amd as sq
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1.5e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x):
+    return x.cuda()
+
+
+def f64(x):
+    return x.detach().to("cpu", torch.float64).numpy()
+
+
+def maxerr(got, want):
+    return float(np.max(np.abs(f64(got) - want))) if np.size(want) else 0.0
+
+
+def rand_inputs(shape, dtype, seed, peaky=False):
+    return tuple(dev(x) for x in inputs.make_qkv(shape, dtype, peaky, seed))
+
+
+# ---------------------------------------------------------------- full forward, small shapes vs full oracle
+
+FORWARD_CASES = [
+    # grid, tile, batch, heads, head_dim, dtype, peaky
+    ((4, 8, 8), (1, 4, 4), 1, 2, 64, torch.float32, False),      # the tiny fp32 configuration's shape
+    ((4, 8, 8), (1, 4, 4), 2, 3, 128, torch.float32, True),
+    ((4, 6, 10), (2, 3, 5), 1, 3, 128, torch.float32, False),    # W = 30, G = 8: ragged key blocks
+    ((4, 6, 10), (2, 3, 5), 2, 3, 128, torch.bfloat16, True),
+    ((8, 8, 8), (2, 4, 4), 1, 2, 64, torch.bfloat16, False),     # W = 32, G = 16
+    ((6, 10, 10), (2, 5, 10), 1, 2, 128, torch.bfloat16, False), # W = 100, G = 6
+    ((8, 12, 10), (1, 12, 10), 1, 2, 128, torch.bfloat16, True), # W = 120, G = 8
+    ((2, 16, 20), (2, 8, 10), 1, 2, 128, torch.bfloat16, False), # W = 160, G = 4
+    ((16, 8, 8), (1, 1, 1), 1, 2, 128, torch.bfloat16, False),   # W = 1, G = 1024
+    ((4, 8, 8), (4, 8, 8), 1, 2, 64, torch.bfloat16, False),     # G = 1: one window
+    ((3, 5, 7), (3, 5, 7), 1, 1, 64, torch.float32, False),      # G = 1, n = 105
+    ((4, 16, 20), (4, 8, 10), 1, 1, 128, torch.bfloat16, True),  # W = 320 (5 chunks of key blocks)
+    ((8, 24, 20), (2, 12, 10), 1, 1, 128, torch.bfloat16, False),# W = 240, G = 16
+]
+
+
+@pytest.mark.parametrize("case", FORWARD_CASES, ids=lambda c: f"{c[0]}-{c[1]}-b{c[2]}h{c[3]}d{c[4]}-{str(c[5])[6:]}")
+def test_forward_matches_oracle(case):
+    grid, tile, B, Hh, d, dtype, peaky = case
+    n = grid[0] * grid[1] * grid[2]
+    q, k, v = rand_inputs((B, n, Hh, d), dtype, 7, peaky)
+    say(f"forward {case}")
+    out = sq.squad_attn_forward(q, k, v, grid, tile, Hh)
+    torch.cuda.synchronize()
+    want = oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)
+    err = maxerr(out, want)
+    say(f"  max-abs {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("case", FORWARD_CASES[:8], ids=lambda c: f"{c[0]}-{c[1]}-{str(c[5])[6:]}")
+def test_each_pass_matches_oracle(case):
+    grid, tile, B, Hh, d, dtype, peaky = case
+    n = grid[0] * grid[1] * grid[2]
+    q, k, v = rand_inputs((B, n, Hh, d), dtype, 8, peaky)
+    o1 = sq.squad_local_pass(q, k, v, grid, tile, Hh)
+    out = sq.squad_global_pass(q, k, v, grid, tile, Hh)   # arbitrary value stream: v itself
+    torch.cuda.synchronize()
+    qq, kk, vv = f64(q), f64(k), f64(v)
+    assert maxerr(o1, oracle.local_pass(qq, kk, vv, grid, tile)) <= TOL[dtype]
+    assert maxerr(out, oracle.global_pass(qq, kk, vv, grid, tile)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16"])
+def test_config_forward_matches_oracle(name):
+    cfg = inputs.CONFIGS[name]
+    q, k, v = (dev(x) for x in inputs.config_inputs(cfg))
+    say(f"config {name}")
+    out = sq.squad_attn_forward(q, k, v, cfg.grid, cfg.tile, cfg.heads)
+    torch.cuda.synchronize()
+    want = oracle.squad_forward(f64(q), f64(k), f64(v), cfg.grid, cfg.tile)
+    err = maxerr(out, want)
+    say(f"  max-abs {err:.3e} (max |out| {np.abs(want).max():.3f})")
+    assert err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("seed", range(1, 10))
+def test_config_seed_sweep(seed):
+    """The tiny and small configurations over more seeds."""
+    for name in ("tiny_fp32", "small_bf16"):
+        cfg = inputs.CONFIGS[name]
+        q, k, v = (dev(x) for x in inputs.config_inputs(cfg, seed=seed))
+        out = sq.squad_attn_forward(q, k, v, cfg.grid, cfg.tile, cfg.heads)
+        torch.cuda.synchronize()
+        if name == "small_bf16":   # the full oracle at 24 heads costs a few seconds; check 4 heads
+            hs = [0, 7, 13, 23]
+            want = oracle.squad_forward(f64(q[:, :, hs]), f64(k[:, :, hs]), f64(v[:, :, hs]), cfg.grid, cfg.tile)
+            err = maxerr(out[:, :, hs], want)
+        else:
+            err = maxerr(out, oracle.squad_forward(f64(q), f64(k), f64(v), cfg.grid, cfg.tile))
+        assert err <= TOL[cfg.dtype], (name, seed, err)
+
+
+# ---------------------------------------------------------------- full-size configurations, sampled
+
+@pytest.mark.parametrize("name", ["dit5b_bf16", "long_bf16", "highres_bf16"])
+def test_large_config_sampled_groups(name):
+    """At full size the oracle computes whole offset groups (every token of the group,
+    each through its own window) for a sample of groups and heads."""
+    cfg = inputs.CONFIGS[name]
+    say(f"config {name}: generating inputs")
+    qc, kc, vc = inputs.config_inputs(cfg)
+    q, k, v = dev(qc), dev(kc), dev(vc)
+    say("  running the forward")
+    out = sq.squad_attn_forward(q, k, v, cfg.grid, cfg.tile, cfg.heads)
+    torch.cuda.synchronize()
+    W = cfg.window
+    offsets = [0, 1, W // 2, W - 1]
+    hs = [0, cfg.heads // 2, cfg.heads - 1]
+    say("  oracle on sampled groups")
+    tokens, want = oracle.squad_forward_groups(qc[:, :, hs].double().numpy(), kc[:, :, hs].double().numpy(),
+                                               vc[:, :, hs].double().numpy(), cfg.grid, cfg.tile, offsets)
+    got = out[:, torch.from_numpy(tokens.reshape(-1)).cuda()][:, :, hs]
+    got = got.reshape(cfg.batch, len(offsets), -1, len(hs), cfg.head_dim)
+    err = maxerr(got, want)
+    say(f"  max-abs {err:.3e} over {want.size} outputs")
+    assert err <= TOL[cfg.dtype]
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- properties at full size (no oracle)
+
+def test_highres_properties():
+    cfg = inputs.CONFIGS["highres_bf16"]
+    qc, kc, vc = inputs.config_inputs(cfg)
+    q, k, v = dev(qc), dev(kc), dev(vc)
+    g, t = cfg.grid, cfg.tile
+    ws = torch.empty(sq.squad_attn_workspace_size(g, t, cfg.heads, 1, 128, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    out = sq.squad_attn_forward(q, k, v, g, t, workspace=ws)
+    # determinism: a second run is bit-identical
+    out2 = sq.squad_attn_forward(q, k, v, g, t, workspace=ws)
+    assert torch.equal(out, out2)
+    # linear in v: doubling v doubles the output (exactly, except where the fp16 local
+    # output is subnormal, below 6.1e-5, and doubling it is not exact)
+    out3 = sq.squad_attn_forward(q, k, v * 2, g, t, workspace=ws)
+    two = 2 * out.float()
+    assert float(((out3.float() - two).abs() - two.abs() * 2.0 ** -7).max()) <= 1e-6   # within one bf16 ulp
+    assert float((out3 == 2 * out).float().mean()) > 0.99
+    del out2, out3
+    # constant values give that constant back
+    ones = torch.full_like(v, 1.0)
+    oc = sq.squad_attn_forward(q, k, ones, g, t, workspace=ws)
+    assert float((oc.float() - 1).abs().max()) <= TOL[torch.bfloat16]
+    del oc, ones
+    # q = 0: the output is the mean of v over all tokens, per head
+    oz = sq.squad_attn_forward(torch.zeros_like(q), k, v, g, t, workspace=ws)
+    mean = v.float().mean(dim=1, keepdim=True)
+    assert float((oz.float() - mean).abs().max()) <= TOL[torch.bfloat16]
+    del oz
+    # a roll of the grid by one tile along each axis rolls the output the same way
+    shp = (1, *g, cfg.heads, 128)
+    for ax in range(3):
+        sh = t[ax]
+        roll = lambda x: torch.roll(x.reshape(shp), sh, dims=1 + ax).reshape(x.shape).contiguous()
+        orl = sq.squad_attn_forward(roll(q), roll(k), roll(v), g, t, workspace=ws)
+        assert float((orl.float() - roll(out).float()).abs().max()) <= TOL[torch.bfloat16]
+        del orl
+
+
+# ---------------------------------------------------------------- the engine and the comparator
+
+@pytest.mark.parametrize("L", [1, 17, 64, 100, 160, 480, 512, 600])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
+def test_window_attn_matches_oracle(L, dtype, d):
+    U = 40
+    g = torch.Generator().manual_seed(L)
+    q, k, v = (torch.randn(U, L, d, generator=g).to(dtype).cuda() for _ in range(3))
+    o = sq.squad_window_attn(q, k, v)
+    torch.cuda.synchronize()
+    assert maxerr(o, oracle.window_attn(f64(q), f64(k), f64(v))) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("n,dtype", [(1024, torch.bfloat16), (1000, torch.bfloat16), (333, torch.float32)])
+def test_dense_matches_oracle(n, dtype):
+    q, k, v = rand_inputs((2, n, 3, 128), dtype, 9)
+    o = sq.squad_dense_attn_forward(q, k, v)
+    torch.cuda.synchronize()
+    assert maxerr(o, oracle.dense_attention(f64(q), f64(k), f64(v))) <= TOL[dtype]
+
+
+def test_single_window_equals_dense_kernel():
+    """tile = grid: SQuad reduces to full attention; compare with the dense kernel."""
+    grid = (4, 16, 16)
+    q, k, v = rand_inputs((1, 1024, 2, 128), torch.bfloat16, 10)
+    a = sq.squad_attn_forward(q, k, v, grid, grid)
+    b = sq.squad_dense_attn_forward(q, k, v)
+    torch.cuda.synchronize()
+    assert float((a.float() - b.float()).abs().max()) <= TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- permutations: bit-exact
+
+PERM_CASES = [((4, 8, 8), (1, 4, 4), 2, 3, 64, torch.bfloat16), ((2, 4, 6), (2, 2, 3), 1, 2, 128, torch.float32),
+              ((32, 24, 40), (2, 8, 10), 1, 24, 128, torch.bfloat16), ((4, 6, 10), (1, 1, 1), 1, 2, 64, torch.float32),
+              ((4, 6, 10), (4, 6, 10), 1, 2, 128, torch.bfloat16)]
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"{c[0]}-{c[1]}")
+def test_permutations_are_exact(case):
+    grid, tile, B, Hh, d, dtype = case
+    n = grid[0] * grid[1] * grid[2]
+    x = torch.randn(B, n, Hh, d).to(dtype)
+    xg = x.cuda()
+    w = sq.squad_tile_gather(xg, grid, tile)
+    want_w = oracle.tile_gather(x.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy(), grid, tile)
+    as_int = lambda t: t.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy()
+    assert np.array_equal(as_int(w), want_w)
+    back = sq.squad_tile_scatter(w, grid, tile)
+    assert torch.equal(back, xg)
+    grp = sq.squad_window_to_group(w, grid, tile)
+    assert np.array_equal(as_int(grp), oracle.window_to_group(want_w))
+
+
+def test_forward_halves_compose_to_the_forward():
+    """squad_attn_forward == squad_attn_forward_local then squad_attn_forward_global, bit for bit."""
+    grid, tile = (8, 12, 10), (2, 6, 5)
+    q, k, v = rand_inputs((2, 960, 3, 128), torch.bfloat16, 11, True)
+    out = sq.squad_attn_forward(q, k, v, grid, tile)
+    ws = sq.squad_attn_forward_local(q, k, v, grid, tile)
+    out2 = sq.squad_attn_forward_global(q, k, grid, tile, ws)
+    assert torch.equal(out, out2)
+    # the workspace holds the local output, group-major [B, heads, Wn, G, d], in fp16
+    o1 = ws.view(torch.float16).reshape(2, 3, 60, 16, 128)
+    want = oracle.tile_gather(oracle.local_pass(f64(q), f64(k), f64(v), grid, tile), grid, tile)
+    assert maxerr(o1.transpose(2, 3), want) <= 1e-2
