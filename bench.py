@@ -173,8 +173,8 @@ def main():
         "forward_events_ms": ms_fwd,
     }
     dom = "local" if ms_local >= ms_global else "global"
-    dom_name = {"local": "attn_bf16_kernel<128,4,bf16,fp16> (local pass)",
-                "global": "attn_bf16_kernel<128,4,fp16,bf16> (global pass)"}[dom]
+    dom_name = {"local": "attn16_kernel<128,4,bf16,fp16> (local pass)",
+                "global": "attn16_kernel<128,4,fp16,bf16> (global pass)"}[dom]
     achieved = kernels[dom]["gbs"]
     digest = kernel_source_digest()
     traffic = traffic_from_profiles(dom, digest)

@@ -1,21 +1,39 @@
-// attn_bf16.hip - the bf16 attention engine behind both SQuad passes (gfx950 MFMA).
+// attn_bf16.hip - the 16-bit attention engine behind both SQuad passes (gfx950 MFMA).
 //
 // One workgroup runs one query chunk (32 rows per wave) of one unit (a window in
 // the local pass, an offset group in the global pass) against all of the unit's
-// keys, streamed through LDS in blocks of 64 keys with an online softmax.  The
+// keys, streamed through LDS in blocks of 32 keys with an online softmax.  The
 // standard softmax of both passes (technical summary, "1. SQuad-Attention
 // Operator") is computed exactly: row max, exp2 of the shifted logits, row sum and
 // a final division, in fp32.
 //
-// Products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
-//   S^T = K * Q^T   (A = 32 keys x 16 dims from LDS, B = Q^T from registers)
-//   O^T = V^T * P^T (A = V^T read with ds_read_b64_tr_b16, B = P^T from registers)
+// Products run on 32x32x16 MFMAs with fp32 accumulation:
+//   S^T = K * Q^T   (A = 32 keys x 16 dims read from LDS, B = Q^T held in registers)
+//   O^T = V^T * P^T (A = V^T read from LDS with ds_read_b64_tr_b16, B = P^T in registers)
 // Computing the transposes puts one query per lane (lane % 32), so the softmax row
-// statistics are per-lane scalars; only the two 32-lane halves of the wave meet, in
-// one cross-half exchange per key block.  The C/D layout of the 32x32 MFMA gives lane
-// l, register r the element (row 8*(r/4) + 4*(l/32) + r%4, column l%32); P^T leaves the
-// S^T registers in exactly the k-slot order the second MFMA needs when V^T is read
-// with the matching key permutation, so P never moves between lanes.
+// statistics are per-lane scalars; the two 32-lane halves of a wave meet once per
+// block.  The C/D layout of the 32x32 MFMA gives lane l, register r the element
+// (row 8*(r/4) + 4*(l/32) + r%4, column l%32); P^T leaves the S^T registers in the
+// k-slot order the second MFMA consumes when V^T is read with the matching key
+// permutation, so P never moves between lanes.
+//
+// Data movement (measured on gfx950: 64 four-byte LDS banks, 256 B per clock):
+//   * K rows go global -> registers -> LDS at a 264-byte pitch; the A operand is
+//     read as two ds_read_b64 per lane, which that pitch keeps free of bank
+//     conflicts.  Two K stages.
+//   * V rows go global -> LDS directly (global_load_lds, 16 B per lane) into a
+//     320-byte pitch (192 B for head_dim 64), which keeps the transposing reads free
+//     of conflicts; the 16-byte pad slots of each row are masked lanes.  Three V
+//     stages, so each block's values are requested two blocks ahead.
+//   * Q rows are loaded straight into the B-operand registers once.
+//   * The output is staged through LDS and stored as whole 16-byte chunks per row.
+// Rows past the end of a unit read the unit's last row (their logits are masked to
+// -inf, so they carry zero weight) and are never stored.
+//
+// The softmax keeps a reference maximum that is raised only when a block's maximum
+// exceeds it by more than 2^8 in the exp2 domain; until then the weights are
+// exp2(logit - reference) <= 256, well inside fp16/bf16 range, and the accumulator
+// needs no rescaling.  The row sum divides it out at the end.
 #include "squad_kernels.h"
 
 namespace squad {
@@ -28,11 +46,11 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BN = 64;  // keys per LDS block
+constexpr int BN = 32;              // keys per block
+constexpr float RESCALE_TAU = 8.f;  // log2 headroom before the reference max is raised
 
-// 16-bit value types of the weights-times-values product: bf16 for bf16 values, fp16
-// for the fp16 local output the global pass reads (see squad_api.hip).
 template <typename T> struct Vec;
 template <> struct Vec<__bf16> {
   typedef bf16x8 x8;
@@ -49,33 +67,49 @@ template <> struct Vec<_Float16> {
   }
 };
 
-__device__ __forceinline__ int64_t shfl64(int64_t x, int src) {
-  int lo = __shfl((int)(uint32_t)(uint64_t)x, src, 64);
-  int hi = __shfl((int)(uint32_t)((uint64_t)x >> 32), src, 64);
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ int shfl(int x, int src) { return __shfl(x, src, 64); }
 
-// VT: type of v (and of the attention weights in the second product); OT: type of out.
+template <int D, int NW>
+struct Cfg {
+  static constexpr int NT = 64 * NW;
+  static constexpr int BM = 32 * NW;
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int KP = D + 4;                    // K / output staging pitch (elements)
+  static constexpr int VP = D == 128 ? 160 : 96;      // V pitch (elements)
+  static constexpr int VSL = VP / 8;                  // 16-byte slots per V row
+  static constexpr int VINS = (BN * VSL + 63) / 64;   // direct-load instructions per V block
+  static constexpr int VPW = (VINS + NW - 1) / NW;    // ... per wave
+  static constexpr int KCH = BN * CPR / NT;           // K chunks per thread per block
+  static constexpr int NVS = 3, NKS = 2;
+  static constexpr int VSTAGE = BN * VP;              // elements
+  static constexpr int KSTAGE = BN * KP;
+  static constexpr int KV_ELEMS = NVS * VSTAGE + NKS * KSTAGE;
+  static constexpr int O_ELEMS = BM * KP;
+  static constexpr int LDS_ELEMS = KV_ELEMS > O_ELEMS ? KV_ELEMS : O_ELEMS;
+  static_assert((VSTAGE * 2) % 1024 == 0, "V stages must be whole 1 KB direct-load blocks");
+  static_assert(BN * CPR % NT == 0, "K staging split");
+  static_assert(VPW * NW * 64 >= BN * VSL, "V staging split");
+};
+
 template <int D, int NW, typename VT, typename OT>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
+  typedef Cfg<D, NW> C;
   typedef typename Vec<VT>::x8 vx8;
   typedef typename Vec<VT>::x4 vx4;
   typedef typename Vec<OT>::x4 ox4;
-  constexpr int NT = 64 * NW;
-  constexpr int BM = 32 * NW;
-  constexpr int KP = D + 8;             // LDS row pitch in elements (272 B for D = 128)
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int KV = BN * KP;           // elements of one K or V buffer
-  constexpr int LDS = (4 * KV > BM * KP) ? 4 * KV : BM * KP;
-  constexpr int RPI = NT / CPR;         // rows one pass of the workgroup covers
-  constexpr int KVI = BN / RPI;         // 16-byte chunks per thread per K (or V) block
-  constexpr int WR = 64 / CPR;          // rows one wave covers per pass
-  constexpr int QI = 32 / WR;           // passes for a wave's 32 rows
-  static_assert(BN % RPI == 0 && 32 % WR == 0, "tiling");
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[LDS];
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::LDS_ELEMS];
+  VT* const vstage = (VT*)smem;                              // NVS stages of BN x VP
+  __bf16* const kstage = smem + C::NVS * C::VSTAGE;          // NKS stages of BN x KP
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -103,69 +137,65 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
 
   const uint32_t L = a.L;
   const uint32_t nkb = (L + BN - 1) / BN;
-  const uint32_t q0 = chunk * BM + wave * 32;   // first query row of this wave
+  const uint32_t q0 = chunk * C::BM + wave * 32;   // first query row of this wave
   const bool active = q0 < L;
 
-  const uint32_t ccol = tid % CPR;              // chunk column for K/V staging
-  const uint32_t crow = tid / CPR;              // row within a staging pass
-  const uint32_t wcol = lane % CPR;             // chunk column for per-wave Q/O passes
-  const uint32_t wrow = lane / CPR;
+  // K staging: thread t owns chunk column t % CPR of rows t / CPR + i * (NT / CPR)
+  const uint32_t kcol = tid % C::CPR;
+  const uint32_t krow = tid / C::CPR;
+  constexpr int KRS = C::NT / C::CPR;
 
-  // ---- K/V block prefetch into registers
-  uint4 kreg[KVI], vreg[KVI];
-  auto prefetch = [&](uint32_t kb) {
-    const uint32_t key = kb * BN + lane;        // lane l locates key row l of the block
-    const bool ok = key < L;
-    const int64_t ok_k = ok ? a.mqk.row_off(key) : -1;
-    const int64_t ok_v = ok ? a.mv.row_off(key) : -1;
-#pragma unroll
-    for (int i = 0; i < KVI; ++i) {
-      const int r = crow + i * RPI;
-      const int64_t ok_ = shfl64(ok_k, r);
-      const int64_t ov_ = shfl64(ok_v, r);
-      uint4 zk = make_uint4(0, 0, 0, 0), zv = zk;
-      if (ok_ >= 0) zk = *(const uint4*)(kg + ok_ + ccol * 8);
-      if (ov_ >= 0) zv = *(const uint4*)(vg + ov_ + ccol * 8);
-      kreg[i] = zk;
-      vreg[i] = zv;
-    }
-  };
-  auto stage = [&](int buf) {
-    __bf16* ks = smem + buf * KV;
-    __bf16* vs = smem + (2 + buf) * KV;
-#pragma unroll
-    for (int i = 0; i < KVI; ++i) {
-      const int r = crow + i * RPI;
-      *(uint4*)(ks + r * KP + ccol * 8) = kreg[i];
-      *(uint4*)(vs + r * KP + ccol * 8) = vreg[i];
-    }
+  // lane l (< 32) locates key l of a block; lanes 32-63 mirror lanes 0-31
+  auto key_offset = [&](const RowMap& m, uint32_t kb) -> int32_t {
+    return m.row_off(min(kb * BN + l32, L - 1));
   };
 
-  // ---- prologue: Q rows of this wave through LDS into MFMA B-operand registers
-  const uint32_t qrow_l = q0 + l32;
-  const int64_t qoff_l = (qrow_l < L) ? a.mqk.row_off(qrow_l) : -1;
-  uint4 qreg[QI];
+  uint4 kreg[C::KCH];
+  auto load_k = [&](int32_t ko) {
 #pragma unroll
-  for (int i = 0; i < QI; ++i) {
-    const int64_t o = shfl64(qoff_l, wrow + i * WR);
-    qreg[i] = make_uint4(0, 0, 0, 0);
-    if (o >= 0) qreg[i] = *(const uint4*)(qg + o + wcol * 8);
-  }
-  prefetch(0);
-  {
-    __bf16* qs = smem + wave * 32 * KP;
+    for (int i = 0; i < C::KCH; ++i) {
+      const int32_t o = shfl(ko, krow + i * KRS);
+      kreg[i] = *(const uint4*)(kg + o + kcol * 8);
+    }
+  };
+  auto store_k = [&](int stage) {
+    __bf16* ks = kstage + stage * C::KSTAGE;
 #pragma unroll
-    for (int i = 0; i < QI; ++i) *(uint4*)(qs + (wrow + i * WR) * KP + wcol * 8) = qreg[i];
-  }
-  __syncthreads();
+    for (int i = 0; i < C::KCH; ++i) {
+      __bf16* p = ks + (krow + i * KRS) * C::KP + kcol * 8;
+      *(uint2*)p = make_uint2(kreg[i].x, kreg[i].y);
+      *(uint2*)(p + 4) = make_uint2(kreg[i].z, kreg[i].w);
+    }
+  };
+  // V: this wave's share of the block's direct loads; slot -> (row slot / VSL, column slot % VSL)
+  auto load_v = [&](int32_t vo, int stage) {
+    VT* vs = vstage + stage * C::VSTAGE;
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const int ins = wave + i * NW;
+      const int slot = ins * 64 + lane;
+      const int row = slot / C::VSL;
+      const int col = slot - row * C::VSL;
+      const int32_t o = shfl(vo, row & 31);
+      if (ins < C::VINS && col < C::CPR && row < BN)
+        __builtin_amdgcn_global_load_lds((const void*)(vg + o + col * 8),
+                                         (lds_void_t*)(vs + ins * 512), 16, 0, 0);
+    }
+  };
+
+  // ---- prologue
   bf16x8 qf[D / 16];
   {
-    const __bf16* qs = smem + wave * 32 * KP + l32 * KP + half * 8;
+    const uint32_t qrow = min(q0 + l32, L - 1);
+    const __bf16* qr = qg + a.mqk.row_off(qrow) + half * 8;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qs + kk * 16);
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
   }
-  __syncthreads();
-  stage(0);
+  load_k(key_offset(a.mqk, 0));
+  load_v(key_offset(a.mv, 0), 0);
+  if (nkb > 1) load_v(key_offset(a.mv, 1), 1);
+  store_k(0);
+  if (nkb > 1) wait_vmcnt<C::VPW>(); else wait_vmcnt<0>();
   __syncthreads();
 
   f32x16 acc[D / 32];
@@ -173,92 +203,97 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-  float m_run = -INFINITY;   // running max of scaled logits (log2 domain)
+  float m_ref = -INFINITY;   // reference max of the scaled logits (log2 domain)
   float l_run = 0.f;         // this lane's partial row sum
   const float c = a.c;
 
+  // transposing-read coordinates of V (see the header comment)
+  const uint32_t trow = 4 * half + ((lane & 15) >> 2);
+  const uint32_t tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  int kst = 0, vst = 0;
   for (uint32_t kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    const bool has_next = kb + 1 < nkb;
-    if (has_next) prefetch(kb + 1);
+    const bool has1 = kb + 1 < nkb;
+    const bool has2 = kb + 2 < nkb;
+    if (has1) load_k(key_offset(a.mqk, kb + 1));
+    if (has2) load_v(key_offset(a.mv, kb + 2), vst == 0 ? 2 : vst - 1);
 
     if (active) {
-      const __bf16* ks = smem + buf * KV;
-      const __bf16* vs = smem + (2 + buf) * KV;
-      // S^T tiles: keys 0-31 and 32-63 of the block against this wave's 32 queries
-      f32x16 s0, s1;
+      const __bf16* ks = kstage + kst * C::KSTAGE + l32 * C::KP + half * 8;
+      f32x16 sc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 k0 = *(const bf16x8*)(ks + l32 * KP + kk * 16 + half * 8);
-        const bf16x8 k1 = *(const bf16x8*)(ks + (32 + l32) * KP + kk * 16 + half * 8);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
+        const uint2 lo = *(const uint2*)(ks + kk * 16);
+        const uint2 hi = *(const uint2*)(ks + kk * 16 + 4);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
       }
       // keys past the end of the unit take no weight
       if ((kb + 1) * BN > L) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t kr = kb * BN + 8 * (r / 4) + 4 * half + (r % 4);
-          if (kr >= L) s0[r] = -INFINITY;
-          if (kr + 32 >= L) s1[r] = -INFINITY;
+          const uint32_t key = kb * BN + 8 * (r / 4) + 4 * half + (r % 4);
+          if (key >= L) sc[r] = -INFINITY;
         }
       }
-      float mx = s0[0];
+      float mx = sc[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx = fmaxf(mx, xhalf(mx)) * c;
+      if (__any(mx > m_ref + RESCALE_TAU)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-      mx = fmaxf(mx, xhalf(mx));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
+      }
       float ps = 0.f;
-      vx8 pb[4];
+      vx8 pb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
-        ps += p0 + p1;
-        pb[r / 8][r % 8] = (VT)p0;
-        pb[2 + r / 8][r % 8] = (VT)p1;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -m_ref));
+        ps += p;
+        pb[r / 8][r % 8] = (VT)p;
       }
-      l_run = l_run * alpha + ps;
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
+      l_run += ps;
       // O^T += V^T P^T, 16 keys per MFMA
-      const uint32_t trow = 4 * half + ((lane & 15) >> 2);
-      const uint32_t tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      const VT* vs = vstage + vst * C::VSTAGE + trow * C::VP + tcol;
 #pragma unroll
-      for (int jk = 0; jk < 4; ++jk) {
+      for (int jk = 0; jk < 2; ++jk) {
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-          const __bf16* p1 = vs + (16 * jk + trow) * KP + mt * 32 + tcol;
-          const __bf16* p2 = p1 + 8 * KP;
-          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(__attribute__((address_space(3))) __bf16*)p1);
-          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(__attribute__((address_space(3))) __bf16*)p2);
-          vx8 va;
+          const VT* p1 = vs + 16 * jk * C::VP + mt * 32;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(__attribute__((address_space(3))) VT*)p1);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(__attribute__((address_space(3))) VT*)(p1 + 8 * C::VP));
           const vx4 lo4 = __builtin_bit_cast(vx4, lo);
           const vx4 hi4 = __builtin_bit_cast(vx4, hi);
+          vx8 va;
           va[0] = lo4[0]; va[1] = lo4[1]; va[2] = lo4[2]; va[3] = lo4[3];
           va[4] = hi4[0]; va[5] = hi4[1]; va[6] = hi4[2]; va[7] = hi4[3];
           acc[mt] = Vec<VT>::mfma(va, pb[jk], acc[mt]);
         }
       }
     }
-    if (has_next) stage(buf ^ 1);
+    if (has1) store_k(kst ^ 1);
+    // this wave's loads of the next V block have landed (only the newest block may be in flight)
+    if (has2) wait_vmcnt<C::VPW>(); else wait_vmcnt<0>();
     __syncthreads();
+    kst ^= 1;
+    vst = vst == 2 ? 0 : vst + 1;
   }
 
   // ---- epilogue: normalise, stage rows in LDS, store 16-byte chunks
   const float inv = 1.f / (l_run + xhalf(l_run));
+  __bf16* const ostage = smem;
   if (active) {
-    __bf16* os = smem + wave * 32 * KP + l32 * KP;
+    OT* os = (OT*)ostage + (wave * 32 + l32) * C::KP;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -273,13 +308,20 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
   if (active) {
-    const int64_t ooff_l = (qrow_l < L) ? a.mo.row_off(qrow_l) : -1;
-    const __bf16* os = smem + wave * 32 * KP;
+    constexpr int WR = 64 / C::CPR;   // rows per wave pass
+    const uint32_t wcol = lane % C::CPR;
+    const uint32_t wrow = lane / C::CPR;
+    const int32_t oo = (q0 + l32 < L) ? a.mo.row_off(q0 + l32) : -1;
+    const OT* os = (const OT*)ostage + wave * 32 * C::KP;
 #pragma unroll
-    for (int i = 0; i < QI; ++i) {
+    for (int i = 0; i < 32 / WR; ++i) {
       const int r = wrow + i * WR;
-      const int64_t o = shfl64(ooff_l, r);
-      if (o >= 0) *(uint4*)(og + o + wcol * 8) = *(const uint4*)(os + r * KP + wcol * 8);
+      const int32_t o = shfl(oo, r);
+      if (o >= 0) {
+        const uint2 lo = *(const uint2*)(os + r * C::KP + wcol * 8);
+        const uint2 hi = *(const uint2*)(os + r * C::KP + wcol * 8 + 4);
+        *(uint4*)(og + o + wcol * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
     }
   }
 }
@@ -289,7 +331,7 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const uint32_t groups = (a.units + 7) / 8;
   const uint64_t blocks = (uint64_t)groups * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, VT, OT>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
+  hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -307,8 +349,7 @@ hipError_t launch_types(const AttnArgs& a, int head_dim, int nw, hipStream_t str
 
 }  // namespace
 
-// Waves per workgroup: 2 for units of at most 64 rows, else 4 (two 4-wave
-// workgroups fit one CU's registers and LDS).
+// Waves per workgroup: 2 for units of at most 64 rows, else 4.
 hipError_t launch_attn_bf16(AttnArgs a, int head_dim, VType vtype, hipStream_t stream) {
   const uint32_t tiles = (a.L + 31) / 32;
   const int nw = tiles > 2 ? 4 : 2;

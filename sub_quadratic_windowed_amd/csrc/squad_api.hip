@@ -57,21 +57,32 @@ Mix mix(uint32_t x1, uint32_t x0, int64_t s2, int64_t s1, int64_t s0) {
 
 Mix linear(int64_t stride) { return mix(1, 1, stride, 0, 0); }
 
-// Token order [B, n, heads, d]: the window part and the offset part of a token index.
-Mix window_part(const Geo& g, int64_t ts) {
-  return mix((uint32_t)g.nh, (uint32_t)g.nw, g.tt * g.H * g.W * ts, g.th * g.W * ts, g.tw * ts);
-}
-Mix offset_part(const Geo& g, int64_t ts) {
-  return mix((uint32_t)g.th, (uint32_t)g.tw, g.H * g.W * ts, g.W * ts, ts);
+Mix32 mix32(uint32_t x1, uint32_t x0, int64_t s2, int64_t s1, int64_t s0) {
+  Mix32 m;
+  m.x1 = FastDiv32(x1);
+  m.x0 = FastDiv32(x0);
+  m.s2 = (int32_t)s2; m.s1 = (int32_t)s1; m.s0 = (int32_t)s0;
+  return m;
 }
 
+Mix32 linear32(int64_t stride) { return mix32(1, 1, stride, 0, 0); }
+
+// Token order [B, n, heads, d]: the window part and the offset part of a token index.
+// (nh, nw, strides) of the window digits and (th, tw, strides) of the offset digits.
 RowMap token_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
   RowMap m;
   const int64_t ts = heads * d;
   m.sB = g.n * ts;
   m.sH = d;
-  m.unit = by_window ? window_part(g, ts) : offset_part(g, ts);
-  m.row = by_window ? offset_part(g, ts) : window_part(g, ts);
+  const int64_t w2 = g.tt * g.H * g.W * ts, w1 = g.th * g.W * ts, w0 = g.tw * ts;
+  const int64_t o2 = g.H * g.W * ts, o1 = g.W * ts, o0 = ts;
+  if (by_window) {
+    m.unit = mix((uint32_t)g.nh, (uint32_t)g.nw, w2, w1, w0);
+    m.row = mix32((uint32_t)g.th, (uint32_t)g.tw, o2, o1, o0);
+  } else {
+    m.unit = mix((uint32_t)g.th, (uint32_t)g.tw, o2, o1, o0);
+    m.row = mix32((uint32_t)g.nh, (uint32_t)g.nw, w2, w1, w0);
+  }
   return m;
 }
 
@@ -81,7 +92,7 @@ RowMap group_major_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
   m.sB = heads * g.Wn * g.G * d;
   m.sH = g.Wn * g.G * d;
   m.unit = by_window ? linear(d) : linear(g.G * d);
-  m.row = by_window ? linear(g.G * d) : linear(d);
+  m.row = by_window ? linear32(g.G * d) : linear32(d);
   return m;
 }
 
@@ -91,7 +102,7 @@ RowMap window_major_map(const Geo& g, int64_t heads, int64_t d, bool by_window) 
   m.sB = heads * g.G * g.Wn * d;
   m.sH = g.G * g.Wn * d;
   m.unit = by_window ? linear(g.Wn * d) : linear(d);
-  m.row = by_window ? linear(d) : linear(g.Wn * d);
+  m.row = by_window ? linear32(d) : linear32(g.Wn * d);
   return m;
 }
 
@@ -130,6 +141,8 @@ int check_grid_call(const int32_t grid[3], const int32_t tile[3], int32_t heads,
   if (st) return st;
   const uint64_t bh = (uint64_t)heads * (uint64_t)batch;
   if (too_many_units(bh, (uint64_t)(g.G > g.Wn ? g.G : g.Wn), bh * (uint64_t)g.n)) return SQUAD_ERR_SHAPE;
+  // the kernels address rows inside one batch element with 32-bit offsets
+  if ((uint64_t)g.n * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   bytes = (size_t)bh * (size_t)g.n * (size_t)head_dim * elem_bytes(dtype);
   return SQUAD_OK;
 }
@@ -371,6 +384,7 @@ int squad_window_attn(const void* q, const void* k, const void* v, void* out, in
   if (units <= 0 || len <= 0) return SQUAD_ERR_INVALID_ARG;
   int st = check_common(1, 1, head_dim, dtype);
   if (st) return st;
+  if ((uint64_t)len * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   const size_t bytes = (size_t)units * (size_t)len * (size_t)head_dim * elem_bytes(dtype);
   const void* in[3] = {q, k, v};
   st = check_ptrs(in, 3, out, bytes);
@@ -380,7 +394,7 @@ int squad_window_attn(const void* q, const void* k, const void* v, void* out, in
   RowMap m;
   m.sB = 0; m.sH = 0;
   m.unit = linear((int64_t)len * head_dim);
-  m.row = linear(head_dim);
+  m.row = linear32(head_dim);
   a.mqk = m; a.mv = m; a.mo = m;
   return run_attn(a, head_dim, dtype, (hipStream_t)stream);
 }
@@ -392,6 +406,7 @@ int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* 
   int st = check_common(heads, batch, head_dim, dtype);
   if (st) return st;
   if ((uint64_t)batch * (uint64_t)heads >= (uint64_t(1) << 32)) return SQUAD_ERR_SHAPE;
+  if ((uint64_t)n * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   const size_t bytes = (size_t)batch * (size_t)n * (size_t)heads * (size_t)head_dim * elem_bytes(dtype);
   const void* in[3] = {q, k, v};
   st = check_ptrs(in, 3, out, bytes);
@@ -402,7 +417,7 @@ int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* 
   m.sB = (int64_t)n * heads * head_dim;
   m.sH = head_dim;
   m.unit = linear(0);
-  m.row = linear((int64_t)heads * head_dim);
+  m.row = linear32((int64_t)heads * head_dim);
   a.mqk = m; a.mv = m; a.mo = m;
   return run_attn(a, head_dim, dtype, (hipStream_t)stream);
 }

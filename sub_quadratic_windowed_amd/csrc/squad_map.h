@@ -48,6 +48,35 @@ struct FastDiv {
   }
 };
 
+// Division by a runtime constant d >= 1 for dividends x < 2^31 with one 32-bit
+// high multiply: with l = ceil(log2 d), m = ceil(2^(31+l) / d) < 2^32 and
+// q = floor(x * m / 2^(31+l)) is exact because x * (m*d - 2^(31+l)) < 2^31 * d
+// <= 2^(31+l) (the same round-up method, for 31-bit dividends).
+struct FastDiv32 {
+  uint32_t mul;    // ceil(2^(31+l) / d); unused for d == 1
+  uint32_t shift;  // l - 1
+  uint32_t d;
+
+  __host__ __device__ FastDiv32() : mul(0), shift(0), d(1) {}
+  __host__ explicit FastDiv32(uint32_t divisor) : mul(0), shift(0), d(divisor) {
+    if (d > 1) {
+      uint32_t l = 0;
+      while ((uint64_t(1) << l) < d) ++l;
+      mul = (uint32_t)(((uint64_t(1) << (31 + l)) + d - 1) / d);
+      shift = l - 1;
+    }
+  }
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t x) const {
+    if (d == 1) return x;
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __umulhi(x, mul) >> shift;
+#else
+    return (uint32_t)(((uint64_t)x * mul) >> 32) >> shift;
+#endif
+  }
+};
+
+// Unit part of a map: evaluated once per workgroup, 64-bit strides.
 struct Mix {
   FastDiv x1, x0;     // radices X1, X0
   int64_t s2, s1, s0; // strides of the digits (elements)
@@ -61,15 +90,30 @@ struct Mix {
   }
 };
 
+// Row part of a map: evaluated per key block in the attention loop, 32-bit (the
+// host guarantees every row offset inside one (batch, head) is below 2^31).
+struct Mix32 {
+  FastDiv32 x1, x0;
+  int32_t s2, s1, s0;
+
+  __host__ __device__ __forceinline__ int32_t at(uint32_t x) const {
+    uint32_t q0 = x0.div(x);
+    uint32_t d0 = x - q0 * x0.d;
+    uint32_t q1 = x1.div(q0);
+    uint32_t d1 = q0 - q1 * x1.d;
+    return (int32_t)(q1 * (uint32_t)s2 + d1 * (uint32_t)s1 + d0 * (uint32_t)s0);
+  }
+};
+
 struct RowMap {
   int64_t sB, sH; // batch and head strides (elements)
   Mix unit;       // unit index -> offset
-  Mix row;        // row index  -> offset
+  Mix32 row;      // row index  -> offset from the unit's base
 
   __host__ __device__ __forceinline__ int64_t base(uint32_t b, uint32_t h, uint32_t s) const {
     return (int64_t)b * sB + (int64_t)h * sH + unit.at(s);
   }
-  __host__ __device__ __forceinline__ int64_t row_off(uint32_t r) const { return row.at(r); }
+  __host__ __device__ __forceinline__ int32_t row_off(uint32_t r) const { return row.at(r); }
 };
 
 }  // namespace squad

@@ -258,4 +258,4 @@ def test_forward_halves_compose_to_the_forward():
     # the workspace holds the local output, group-major [B, heads, Wn, G, d], in fp16
     o1 = ws.view(torch.float16).reshape(2, 3, 60, 16, 128)
     want = oracle.tile_gather(oracle.local_pass(f64(q), f64(k), f64(v), grid, tile), grid, tile)
-    assert maxerr(o1.transpose(2, 3), want) <= 1e-2
+    assert maxerr(o1.transpose(2, 3), want) <= TOL[torch.bfloat16]
