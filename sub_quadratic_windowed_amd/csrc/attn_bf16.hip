@@ -21,10 +21,12 @@
 //   * K rows go global -> registers -> LDS at a 264-byte pitch; the A operand is
 //     read as two ds_read_b64 per lane, which that pitch keeps free of bank
 //     conflicts.  Two K stages.
-//   * V rows go global -> LDS directly (global_load_lds, 16 B per lane) into a
-//     320-byte pitch (192 B for head_dim 64), which keeps the transposing reads free
-//     of conflicts; the 16-byte pad slots of each row are masked lanes.  Three V
-//     stages, so each block's values are requested two blocks ahead.
+//   * V rows go global -> LDS directly (global_load_lds, 16 B per lane).  Each
+//     group of four rows is stored chunk-interleaved: 16-byte chunk c of row r sits
+//     at slot 4*c + r%4 of its group, so the four rows a transposing read touches
+//     cover 16 consecutive slots (all 64 banks) and one direct load fills whole
+//     groups with no idle lanes.  Three V stages, so each block's values are
+//     requested two blocks ahead.
 //   * Q rows are loaded straight into the B-operand registers once.
 //   * The output is staged through LDS and stored as whole 16-byte chunks per row.
 // Rows past the end of a unit read the unit's last row (their logits are masked to
@@ -84,31 +86,31 @@ struct Cfg {
   static constexpr int BM = 32 * NW;
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
   static constexpr int KP = D + 4;                    // K / output staging pitch (elements)
-  static constexpr int VP = D == 128 ? 160 : 96;      // V pitch (elements)
-  static constexpr int VSL = VP / 8;                  // 16-byte slots per V row
-  static constexpr int VINS = (BN * VSL + 63) / 64;   // direct-load instructions per V block
-  static constexpr int VPW = (VINS + NW - 1) / NW;    // ... per wave
+  static constexpr int VGRP = 4 * D;                  // elements of one 4-row V group
+  static constexpr int VINS = BN * CPR / 64;          // direct-load instructions per V block
+  static constexpr int VPW = VINS / NW;               // ... per wave
+  static constexpr int GPI = 64 / (4 * CPR);          // 4-row groups per direct load
   static constexpr int KCH = BN * CPR / NT;           // K chunks per thread per block
   static constexpr int NVS = 3, NKS = 2;
-  static constexpr int VSTAGE = BN * VP;              // elements
+  static constexpr int VSTAGE = BN * D;               // elements
   static constexpr int KSTAGE = BN * KP;
   static constexpr int KV_ELEMS = NVS * VSTAGE + NKS * KSTAGE;
   static constexpr int O_ELEMS = BM * KP;
   static constexpr int LDS_ELEMS = KV_ELEMS > O_ELEMS ? KV_ELEMS : O_ELEMS;
   static_assert((VSTAGE * 2) % 1024 == 0, "V stages must be whole 1 KB direct-load blocks");
   static_assert(BN * CPR % NT == 0, "K staging split");
-  static_assert(VPW * NW * 64 >= BN * VSL, "V staging split");
+  static_assert(VPW * NW == VINS && VINS * 64 == BN * CPR, "V staging split");
 };
 
 template <int D, int NW, typename VT, typename OT>
-__global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(AttnArgs a) {
   typedef Cfg<D, NW> C;
   typedef typename Vec<VT>::x8 vx8;
   typedef typename Vec<VT>::x4 vx4;
   typedef typename Vec<OT>::x4 ox4;
 
   __shared__ __attribute__((aligned(1024))) __bf16 smem[C::LDS_ELEMS];
-  VT* const vstage = (VT*)smem;                              // NVS stages of BN x VP
+  VT* const vstage = (VT*)smem;                              // NVS stages of BN x D
   __bf16* const kstage = smem + C::NVS * C::VSTAGE;          // NKS stages of BN x KP
 
   const uint32_t tid = threadIdx.x;
@@ -149,6 +151,10 @@ __global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
   auto key_offset = [&](const RowMap& m, uint32_t kb) -> int32_t {
     return m.row_off(min(kb * BN + l32, L - 1));
   };
+  const bool v_like_k = a.v_like_k != 0;
+  auto v_offset = [&](uint32_t kb, int32_t ko) -> int32_t {
+    return v_like_k ? ko : key_offset(a.mv, kb);
+  };
 
   uint4 kreg[C::KCH];
   auto load_k = [&](int32_t ko) {
@@ -167,19 +173,18 @@ __global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
       *(uint2*)(p + 4) = make_uint2(kreg[i].z, kreg[i].w);
     }
   };
-  // V: this wave's share of the block's direct loads; slot -> (row slot / VSL, column slot % VSL)
+  // V: this wave's share of the block's direct loads.  Load `ins` fills 4-row groups
+  // GPI * ins ...; lane i carries row 4 * group + i % 4, chunk (i % (4 * CPR)) / 4.
+  const uint32_t vrow0 = 4 * (lane / (4 * C::CPR)) + (lane & 3);
+  const uint32_t vcol = (lane % (4 * C::CPR)) >> 2;
   auto load_v = [&](int32_t vo, int stage) {
     VT* vs = vstage + stage * C::VSTAGE;
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const int ins = wave + i * NW;
-      const int slot = ins * 64 + lane;
-      const int row = slot / C::VSL;
-      const int col = slot - row * C::VSL;
-      const int32_t o = shfl(vo, row & 31);
-      if (ins < C::VINS && col < C::CPR && row < BN)
-        __builtin_amdgcn_global_load_lds((const void*)(vg + o + col * 8),
-                                         (lds_void_t*)(vs + ins * 512), 16, 0, 0);
+      const int32_t o = shfl(vo, 4 * C::GPI * ins + vrow0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg + o + vcol * 8),
+                                       (lds_void_t*)(vs + ins * 512), 16, 0, 0);
     }
   };
 
@@ -191,9 +196,12 @@ __global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
   }
-  load_k(key_offset(a.mqk, 0));
-  load_v(key_offset(a.mv, 0), 0);
-  if (nkb > 1) load_v(key_offset(a.mv, 1), 1);
+  {
+    const int32_t ko = key_offset(a.mqk, 0);
+    load_k(ko);
+    load_v(v_offset(0, ko), 0);
+  }
+  if (nkb > 1) load_v(v_offset(1, key_offset(a.mqk, 1)), 1);
   store_k(0);
   if (nkb > 1) wait_vmcnt<C::VPW>(); else wait_vmcnt<0>();
   __syncthreads();
@@ -207,16 +215,18 @@ __global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
   float l_run = 0.f;         // this lane's partial row sum
   const float c = a.c;
 
-  // transposing-read coordinates of V (see the header comment)
-  const uint32_t trow = 4 * half + ((lane & 15) >> 2);
-  const uint32_t tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // transposing-read coordinates of V: lane l reads keys 4 * half + (l & 15) / 4
+  // (+ 8 for the second read) at dims 16 * ((l >> 4) & 1) + 4 * (l & 3) of each
+  // 32-dim tile, located in the chunk-interleaved groups
+  const uint32_t tdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint32_t toff = half * C::VGRP + 8 * (4 * (tdim >> 3) + ((lane & 15) >> 2)) + (tdim & 7);
 
   int kst = 0, vst = 0;
   for (uint32_t kb = 0; kb < nkb; ++kb) {
     const bool has1 = kb + 1 < nkb;
     const bool has2 = kb + 2 < nkb;
     if (has1) load_k(key_offset(a.mqk, kb + 1));
-    if (has2) load_v(key_offset(a.mv, kb + 2), vst == 0 ? 2 : vst - 1);
+    if (has2) load_v(v_offset(kb + 2, key_offset(a.mqk, kb + 2)), vst == 0 ? 2 : vst - 1);
 
     if (active) {
       const __bf16* ks = kstage + kst * C::KSTAGE + l32 * C::KP + half * 8;
@@ -242,7 +252,9 @@ __global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       mx = fmaxf(mx, xhalf(mx)) * c;
-      if (__any(mx > m_ref + RESCALE_TAU)) {
+      if (kb == 0) {
+        m_ref = mx;
+      } else if (__any(mx > m_ref + RESCALE_TAU)) {
         const float m_new = fmaxf(m_ref, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
         m_ref = m_new;
@@ -262,16 +274,17 @@ __global__ __launch_bounds__(64 * NW) void attn16_kernel(AttnArgs a) {
       }
       l_run += ps;
       // O^T += V^T P^T, 16 keys per MFMA
-      const VT* vs = vstage + vst * C::VSTAGE + trow * C::VP + tcol;
+      const VT* vs = vstage + vst * C::VSTAGE + toff;
 #pragma unroll
       for (int jk = 0; jk < 2; ++jk) {
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-          const VT* p1 = vs + 16 * jk * C::VP + mt * 32;
+          // keys 16 jk + ... are groups 4 jk + half (+2); dims 32 mt + ... are chunks 4 mt + ...
+          const VT* p1 = vs + 4 * jk * C::VGRP + 4 * 8 * 4 * mt;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4_t*)(__attribute__((address_space(3))) VT*)p1);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_t*)(__attribute__((address_space(3))) VT*)(p1 + 8 * C::VP));
+              (lds_s16x4_t*)(__attribute__((address_space(3))) VT*)(p1 + 2 * C::VGRP));
           const vx4 lo4 = __builtin_bit_cast(vx4, lo);
           const vx4 hi4 = __builtin_bit_cast(vx4, hi);
           vx8 va;

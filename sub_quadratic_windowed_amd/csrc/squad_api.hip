@@ -123,6 +123,7 @@ AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, uint32_
 int run_attn(AttnArgs a, int32_t head_dim, int32_t dtype, hipStream_t stream,
              VType vtype = VType::kBf16ToBf16) {
   if (a.units == 0 || a.L == 0) return SQUAD_OK;
+  a.v_like_k = memcmp(&a.mqk.row, &a.mv.row, sizeof(a.mqk.row)) == 0;
   const hipError_t e = dtype == SQUAD_DTYPE_BF16 ? launch_attn_bf16(a, head_dim, vtype, stream)
                                                  : launch_attn_f32(a, head_dim, stream);
   return e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;

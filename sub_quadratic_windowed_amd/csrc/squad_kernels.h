@@ -27,6 +27,7 @@ struct AttnArgs {
   FastDiv fBH, fHeads;
   uint32_t units;    // BH * U
   uint32_t nchunks;  // query chunks per unit (set by the launcher)
+  uint32_t v_like_k; // nonzero: mv locates rows exactly as mqk does
   float c;           // softmax scale * log2(e)
 };
 
