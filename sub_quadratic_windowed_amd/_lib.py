@@ -4,7 +4,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsquad.so")
+# SQUAD_LIBRARY may point at another build of the same C ABI (for A/B comparisons)
+LIB_PATH = os.environ.get("SQUAD_LIBRARY") or os.path.join(_HERE, "libsquad.so")
 
 STATUS_NAMES = {
     0: "SQUAD_OK",

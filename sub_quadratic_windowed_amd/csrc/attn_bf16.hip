@@ -18,9 +18,11 @@
 // permutation, so P never moves between lanes.
 //
 // Data movement (measured on gfx950: 64 four-byte LDS banks, 256 B per clock):
-//   * K rows go global -> registers -> LDS at a 264-byte pitch; the A operand is
-//     read as two ds_read_b64 per lane, which that pitch keeps free of bank
-//     conflicts.  Two K stages.
+//   * K rows go global -> LDS directly as well, 16-byte chunk c of row r at slot
+//     c ^ (r % CPR) of the row (an XOR swizzle, CPR = chunks per row), and the A
+//     operand is read as two ds_read_b64 per lane (two-way bank conflicts: the 32
+//     rows a read touches share 16 slot columns).  Three K stages, two blocks ahead,
+//     with no staging registers.
 //   * V rows go global -> LDS directly (global_load_lds, 16 B per lane).  Each
 //     group of four rows is stored chunk-interleaved: 16-byte chunk c of row r sits
 //     at slot 4*c + r%4 of its group, so the four rows a transposing read touches
@@ -90,15 +92,14 @@ struct Cfg {
   static constexpr int VINS = BN * CPR / 64;          // direct-load instructions per V block
   static constexpr int VPW = VINS / NW;               // ... per wave
   static constexpr int GPI = 64 / (4 * CPR);          // 4-row groups per direct load
-  static constexpr int KCH = BN * CPR / NT;           // K chunks per thread per block
-  static constexpr int NVS = 3, NKS = 2;
+  static constexpr int KRPI = 64 / CPR;               // K rows per direct load
+  static constexpr int NST = 3;                       // K and V stages
   static constexpr int VSTAGE = BN * D;               // elements
-  static constexpr int KSTAGE = BN * KP;
-  static constexpr int KV_ELEMS = NVS * VSTAGE + NKS * KSTAGE;
+  static constexpr int KSTAGE = BN * D;
+  static constexpr int KV_ELEMS = NST * (VSTAGE + KSTAGE);
   static constexpr int O_ELEMS = BM * KP;
   static constexpr int LDS_ELEMS = KV_ELEMS > O_ELEMS ? KV_ELEMS : O_ELEMS;
   static_assert((VSTAGE * 2) % 1024 == 0, "V stages must be whole 1 KB direct-load blocks");
-  static_assert(BN * CPR % NT == 0, "K staging split");
   static_assert(VPW * NW == VINS && VINS * 64 == BN * CPR, "V staging split");
 };
 
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   typedef typename Vec<OT>::x4 ox4;
 
   __shared__ __attribute__((aligned(1024))) __bf16 smem[C::LDS_ELEMS];
-  VT* const vstage = (VT*)smem;                              // NVS stages of BN x D
-  __bf16* const kstage = smem + C::NVS * C::VSTAGE;          // NKS stages of BN x KP
+  VT* const vstage = (VT*)smem;                              // NST stages of BN x D
+  __bf16* const kstage = smem + C::NST * C::VSTAGE;          // NST stages of BN x D
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -142,11 +143,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   const uint32_t q0 = chunk * C::BM + wave * 32;   // first query row of this wave
   const bool active = q0 < L;
 
-  // K staging: thread t owns chunk column t % CPR of rows t / CPR + i * (NT / CPR)
-  const uint32_t kcol = tid % C::CPR;
-  const uint32_t krow = tid / C::CPR;
-  constexpr int KRS = C::NT / C::CPR;
-
   // lane l (< 32) locates key l of a block; lanes 32-63 mirror lanes 0-31
   auto key_offset = [&](const RowMap& m, uint32_t kb) -> int32_t {
     return m.row_off(min(kb * BN + l32, L - 1));
@@ -156,21 +152,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     return v_like_k ? ko : key_offset(a.mv, kb);
   };
 
-  uint4 kreg[C::KCH];
-  auto load_k = [&](int32_t ko) {
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int32_t o = shfl(ko, krow + i * KRS);
-      kreg[i] = *(const uint4*)(kg + o + kcol * 8);
-    }
-  };
-  auto store_k = [&](int stage) {
+  // K: this wave's share of the block's direct loads.  Load `ins` fills rows
+  // KRPI * ins ...; lane i carries row KRPI * ins + i / CPR, stored slot i % CPR,
+  // i.e. chunk (i % CPR) ^ (row % CPR).
+  const uint32_t krow0 = lane / C::CPR;
+  const uint32_t kslot = lane % C::CPR;
+  auto load_k = [&](int32_t ko, int stage) {
     __bf16* ks = kstage + stage * C::KSTAGE;
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      __bf16* p = ks + (krow + i * KRS) * C::KP + kcol * 8;
-      *(uint2*)p = make_uint2(kreg[i].x, kreg[i].y);
-      *(uint2*)(p + 4) = make_uint2(kreg[i].z, kreg[i].w);
+    for (int i = 0; i < C::VPW; ++i) {
+      const int ins = wave + i * NW;
+      const uint32_t row = C::KRPI * ins + krow0;
+      const int32_t o = shfl(ko, row);
+      const uint32_t chunk = kslot ^ (row & (C::CPR - 1));
+      __builtin_amdgcn_global_load_lds((const void*)(kg + o + chunk * 8),
+                                       (lds_void_t*)(ks + ins * 512), 16, 0, 0);
     }
   };
   // V: this wave's share of the block's direct loads.  Load `ins` fills 4-row groups
@@ -198,12 +194,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   }
   {
     const int32_t ko = key_offset(a.mqk, 0);
-    load_k(ko);
+    load_k(ko, 0);
     load_v(v_offset(0, ko), 0);
   }
-  if (nkb > 1) load_v(v_offset(1, key_offset(a.mqk, 1)), 1);
-  store_k(0);
-  if (nkb > 1) wait_vmcnt<C::VPW>(); else wait_vmcnt<0>();
+  if (nkb > 1) {
+    const int32_t ko = key_offset(a.mqk, 1);
+    load_k(ko, 1);
+    load_v(v_offset(1, ko), 1);
+    wait_vmcnt<2 * C::VPW>();
+  } else {
+    wait_vmcnt<0>();
+  }
   __syncthreads();
 
   f32x16 acc[D / 32];
@@ -221,22 +222,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   const uint32_t tdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const uint32_t toff = half * C::VGRP + 8 * (4 * (tdim >> 3) + ((lane & 15) >> 2)) + (tdim & 7);
 
-  int kst = 0, vst = 0;
+  // the A operand of the scores: row l32, logical chunk 2 kk + half, stored at
+  // slot (2 kk + half) ^ (l32 % CPR)
+  const uint32_t kxor = l32 & (C::CPR - 1);
+  int vst = 0;
   for (uint32_t kb = 0; kb < nkb; ++kb) {
-    const bool has1 = kb + 1 < nkb;
     const bool has2 = kb + 2 < nkb;
-    if (has1) load_k(key_offset(a.mqk, kb + 1));
-    if (has2) load_v(v_offset(kb + 2, key_offset(a.mqk, kb + 2)), vst == 0 ? 2 : vst - 1);
+    if (has2) {
+      const int32_t ko = key_offset(a.mqk, kb + 2);
+      const int st2 = vst == 0 ? 2 : vst - 1;
+      load_k(ko, st2);
+      load_v(v_offset(kb + 2, ko), st2);
+    }
 
     if (active) {
-      const __bf16* ks = kstage + kst * C::KSTAGE + l32 * C::KP + half * 8;
+      const __bf16* ks = kstage + vst * C::KSTAGE + l32 * D;
       f32x16 sc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const uint2 lo = *(const uint2*)(ks + kk * 16);
-        const uint2 hi = *(const uint2*)(ks + kk * 16 + 4);
+        const __bf16* kp = ks + (((2 * kk + half) ^ kxor) << 3);
+        const uint2 lo = *(const uint2*)kp;
+        const uint2 hi = *(const uint2*)(kp + 4);
         const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
       }
@@ -294,11 +302,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         }
       }
     }
-    if (has1) store_k(kst ^ 1);
-    // this wave's loads of the next V block have landed (only the newest block may be in flight)
-    if (has2) wait_vmcnt<C::VPW>(); else wait_vmcnt<0>();
+    // this wave's loads of block kb + 1 have landed (only block kb + 2 may be in flight)
+    if (has2) wait_vmcnt<2 * C::VPW>(); else wait_vmcnt<0>();
     __syncthreads();
-    kst ^= 1;
     vst = vst == 2 ? 0 : vst + 1;
   }
 

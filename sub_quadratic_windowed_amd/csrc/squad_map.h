@@ -52,26 +52,28 @@ struct FastDiv {
 // high multiply: with l = ceil(log2 d), m = ceil(2^(31+l) / d) < 2^32 and
 // q = floor(x * m / 2^(31+l)) is exact because x * (m*d - 2^(31+l)) < 2^31 * d
 // <= 2^(31+l) (the same round-up method, for 31-bit dividends).
+// d == 1 is folded in without a branch: mul = 0, pass = all ones, shift = 0.
 struct FastDiv32 {
-  uint32_t mul;    // ceil(2^(31+l) / d); unused for d == 1
+  uint32_t mul;    // ceil(2^(31+l) / d)
+  uint32_t pass;   // ~0u for d == 1, else 0
   uint32_t shift;  // l - 1
   uint32_t d;
 
-  __host__ __device__ FastDiv32() : mul(0), shift(0), d(1) {}
-  __host__ explicit FastDiv32(uint32_t divisor) : mul(0), shift(0), d(divisor) {
+  __host__ __device__ FastDiv32() : mul(0), pass(~0u), shift(0), d(1) {}
+  __host__ explicit FastDiv32(uint32_t divisor) : mul(0), pass(~0u), shift(0), d(divisor) {
     if (d > 1) {
       uint32_t l = 0;
       while ((uint64_t(1) << l) < d) ++l;
       mul = (uint32_t)(((uint64_t(1) << (31 + l)) + d - 1) / d);
       shift = l - 1;
+      pass = 0;
     }
   }
   __host__ __device__ __forceinline__ uint32_t div(uint32_t x) const {
-    if (d == 1) return x;
 #if defined(__HIP_DEVICE_COMPILE__)
-    return __umulhi(x, mul) >> shift;
+    return (__umulhi(x, mul) + (x & pass)) >> shift;
 #else
-    return (uint32_t)(((uint64_t)x * mul) >> 32) >> shift;
+    return ((uint32_t)(((uint64_t)x * mul) >> 32) + (x & pass)) >> shift;
 #endif
   }
 };
