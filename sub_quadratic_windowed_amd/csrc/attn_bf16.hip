@@ -79,6 +79,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most 2 * n direct loads (this wave's K and V loads of the newest
+// block) are outstanding; n is wave-uniform and at most 4.
+__device__ __forceinline__ void wait_newest(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<2>(); break;
+    case 2: wait_vmcnt<4>(); break;
+    case 3: wait_vmcnt<6>(); break;
+    default: wait_vmcnt<8>(); break;
+  }
+}
+
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ int shfl(int x, int src) { return __shfl(x, src, 64); }
 
@@ -87,20 +99,28 @@ struct Cfg {
   static constexpr int NT = 64 * NW;
   static constexpr int BM = 32 * NW;
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int KP = D + 4;                    // K / output staging pitch (elements)
   static constexpr int VGRP = 4 * D;                  // elements of one 4-row V group
-  static constexpr int VINS = BN * CPR / 64;          // direct-load instructions per V block
-  static constexpr int VPW = VINS / NW;               // ... per wave
+  static constexpr int VINS = BN * CPR / 64;          // direct loads per K (or V) block
+  static constexpr int VPW = (VINS + NW - 1) / NW;    // ... at most per wave
   static constexpr int GPI = 64 / (4 * CPR);          // 4-row groups per direct load
   static constexpr int KRPI = 64 / CPR;               // K rows per direct load
-  static constexpr int NST = 3;                       // K and V stages
-  static constexpr int VSTAGE = BN * D;               // elements
-  static constexpr int KSTAGE = BN * D;
-  static constexpr int KV_ELEMS = NST * (VSTAGE + KSTAGE);
-  static constexpr int O_ELEMS = BM * KP;
-  static constexpr int LDS_ELEMS = KV_ELEMS > O_ELEMS ? KV_ELEMS : O_ELEMS;
-  static_assert((VSTAGE * 2) % 1024 == 0, "V stages must be whole 1 KB direct-load blocks");
-  static_assert(VPW * NW == VINS && VINS * 64 == BN * CPR, "V staging split");
+  static_assert((BN * D * 2) % 1024 == 0, "stages must be whole 1 KB direct-load blocks");
+  static_assert(VINS * 64 == BN * CPR, "K/V staging split");
+};
+
+// One LDS stage of K (or V): 32 rows x D 16-bit elements.  Each stage is its own
+// __shared__ object so the compiler can tell the stage being read from the stages
+// whose direct loads are still in flight (no blanket vmcnt(0) before every read).
+template <int D, int I>
+struct Stage {
+  static __device__ __forceinline__ __bf16* k() {
+    __shared__ __attribute__((aligned(1024))) __bf16 buf[BN * D];
+    return buf;
+  }
+  static __device__ __forceinline__ __bf16* v() {
+    __shared__ __attribute__((aligned(1024))) __bf16 buf[BN * D];
+    return buf;
+  }
 };
 
 template <int D, int NW, typename VT, typename OT>
@@ -110,13 +130,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   typedef typename Vec<VT>::x4 vx4;
   typedef typename Vec<OT>::x4 ox4;
 
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[C::LDS_ELEMS];
-  VT* const vstage = (VT*)smem;                              // NST stages of BN x D
-  __bf16* const kstage = smem + C::NST * C::VSTAGE;          // NST stages of BN x D
-
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t wave = tid >> 6;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t half = lane >> 5;
   const uint32_t l32 = lane & 31;
 
@@ -157,34 +173,53 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // i.e. chunk (i % CPR) ^ (row % CPR).
   const uint32_t krow0 = lane / C::CPR;
   const uint32_t kslot = lane % C::CPR;
-  auto load_k = [&](int32_t ko, int stage) {
-    __bf16* ks = kstage + stage * C::KSTAGE;
-#pragma unroll
-    for (int i = 0; i < C::VPW; ++i) {
-      const int ins = wave + i * NW;
-      const uint32_t row = C::KRPI * ins + krow0;
-      const int32_t o = shfl(ko, row);
-      const uint32_t chunk = kslot ^ (row & (C::CPR - 1));
-      __builtin_amdgcn_global_load_lds((const void*)(kg + o + chunk * 8),
-                                       (lds_void_t*)(ks + ins * 512), 16, 0, 0);
+  // direct loads this wave issues per block, for K and for V each
+  const int my_loads = __builtin_amdgcn_readfirstlane((C::VINS - (int)wave + NW - 1) / NW);
+  // wait until only this wave's loads of the newest block may be in flight
+  auto wait_loads = [&](bool newest_in_flight) {
+    if (!newest_in_flight) {
+      wait_vmcnt<0>();
+    } else if constexpr (C::VINS % NW == 0) {
+      wait_vmcnt<2 * (C::VINS / NW)>();
+    } else {
+      wait_newest(my_loads);
     }
   };
-  // V: this wave's share of the block's direct loads.  Load `ins` fills 4-row groups
-  // GPI * ins ...; lane i carries row 4 * group + i % 4, chunk (i % (4 * CPR)) / 4.
+  // V: load `ins` fills 4-row groups GPI * ins ...; lane i carries row
+  // 4 * group + i % 4, chunk (i % (4 * CPR)) / 4.
   const uint32_t vrow0 = 4 * (lane / (4 * C::CPR)) + (lane & 3);
   const uint32_t vcol = (lane % (4 * C::CPR)) >> 2;
-  auto load_v = [&](int32_t vo, int stage) {
-    VT* vs = vstage + stage * C::VSTAGE;
+  // Loads of one block are prepared (row offsets located, lanes' 32-bit element
+  // offsets formed) one step before they are issued, so the shuffles and the
+  // address arithmetic stay off the path between a block's barrier and its MFMAs.
+  int32_t pk[C::VPW], pv[C::VPW];
+  auto prep_block = [&](uint32_t kb) {
+    const int32_t ko = key_offset(a.mqk, kb);
+    const int32_t vo = v_offset(kb, ko);
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const int ins = wave + i * NW;
-      const int32_t o = shfl(vo, 4 * C::GPI * ins + vrow0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg + o + vcol * 8),
-                                       (lds_void_t*)(vs + ins * 512), 16, 0, 0);
+      const uint32_t krow = C::KRPI * ins + krow0;
+      const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
+      pk[i] = shfl(ko, krow & 31) + (int32_t)(kchunk * 8);
+      pv[i] = shfl(vo, (4 * C::GPI * ins + vrow0) & 31) + (int32_t)(vcol * 8);
+    }
+  };
+  // the prepared block's K and V rows into stage ST
+  auto issue_block = [&](auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    __bf16* ks = Stage<D, ST>::k();
+    VT* vs = (VT*)Stage<D, ST>::v();
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const int ins = wave + i * NW;
+      if (C::VPW * NW != C::VINS && ins >= C::VINS) break;
+      __builtin_amdgcn_global_load_lds((const void*)(kg + pk[i]), (lds_void_t*)(ks + ins * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg + pv[i]), (lds_void_t*)(vs + ins * 512), 16, 0, 0);
     }
   };
 
-  // ---- prologue
+  // ---- prologue: Q registers; blocks 0 and 1 requested
   bf16x8 qf[D / 16];
   {
     const uint32_t qrow = min(q0 + l32, L - 1);
@@ -192,20 +227,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
   }
-  {
-    const int32_t ko = key_offset(a.mqk, 0);
-    load_k(ko, 0);
-    load_v(v_offset(0, ko), 0);
-  }
+  prep_block(0);
+  issue_block(std::integral_constant<int, 0>{});
   if (nkb > 1) {
-    const int32_t ko = key_offset(a.mqk, 1);
-    load_k(ko, 1);
-    load_v(v_offset(1, ko), 1);
-    wait_vmcnt<2 * C::VPW>();
-  } else {
-    wait_vmcnt<0>();
+    prep_block(1);
+    issue_block(std::integral_constant<int, 1>{});
   }
-  __syncthreads();
+  if (nkb > 2) prep_block(2);
+  wait_loads(nkb > 1);
+  __builtin_amdgcn_s_barrier();
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -221,22 +251,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // 32-dim tile, located in the chunk-interleaved groups
   const uint32_t tdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const uint32_t toff = half * C::VGRP + 8 * (4 * (tdim >> 3) + ((lane & 15) >> 2)) + (tdim & 7);
-
   // the A operand of the scores: row l32, logical chunk 2 kk + half, stored at
   // slot (2 kk + half) ^ (l32 % CPR)
   const uint32_t kxor = l32 & (C::CPR - 1);
-  int vst = 0;
-  for (uint32_t kb = 0; kb < nkb; ++kb) {
+
+  // one key block held in stage ST; requests block kb + 2 into stage (ST + 2) % 3
+  auto step = [&](uint32_t kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
     const bool has2 = kb + 2 < nkb;
-    if (has2) {
-      const int32_t ko = key_offset(a.mqk, kb + 2);
-      const int st2 = vst == 0 ? 2 : vst - 1;
-      load_k(ko, st2);
-      load_v(v_offset(kb + 2, ko), st2);
-    }
+    if (has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
 
     if (active) {
-      const __bf16* ks = kstage + vst * C::KSTAGE + l32 * D;
+      const __bf16* ks = Stage<D, ST>::k() + l32 * D;
       f32x16 sc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -282,7 +308,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       }
       l_run += ps;
       // O^T += V^T P^T, 16 keys per MFMA
-      const VT* vs = vstage + vst * C::VSTAGE + toff;
+      const VT* vs = (const VT*)Stage<D, ST>::v() + toff;
 #pragma unroll
       for (int jk = 0; jk < 2; ++jk) {
 #pragma unroll
@@ -302,17 +328,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         }
       }
     }
-    // this wave's loads of block kb + 1 have landed (only block kb + 2 may be in flight)
-    if (has2) wait_vmcnt<2 * C::VPW>(); else wait_vmcnt<0>();
-    __syncthreads();
-    vst = vst == 2 ? 0 : vst + 1;
+    if (kb + 3 < nkb) prep_block(kb + 3);
+    // this wave's loads of block kb + 1 have landed (only block kb + 2 may be in
+    // flight); the barrier then publishes them and retires stage ST's readers
+    wait_loads(has2);
+    __builtin_amdgcn_s_barrier();
+  };
+  for (uint32_t kb = 0; kb < nkb; kb += 3) {
+    step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
+    if (kb + 2 < nkb) step(kb + 2, std::integral_constant<int, 2>{});
   }
 
-  // ---- epilogue: normalise, stage rows in LDS, store 16-byte chunks
-  const float inv = 1.f / (l_run + xhalf(l_run));
-  __bf16* const ostage = smem;
+  // ---- epilogue: normalise; each wave stages its 32 rows in a free stage buffer
+  // (chunk c of row r at slot c ^ (r % CPR)) and stores them as 16-byte chunks
+  OT* ostage = (OT*)(wave == 0 ? Stage<D, 0>::k() : wave == 1 ? Stage<D, 1>::k()
+                     : wave == 2 ? Stage<D, 2>::k() : Stage<D, 0>::v());
+  if (NW > 4) ostage = nullptr;  // (only 2- and 4-wave workgroups are launched)
   if (active) {
-    OT* os = (OT*)ostage + (wave * 32 + l32) * C::KP;
+    const float inv = 1.f / (l_run + xhalf(l_run));
+    OT* orow = ostage + l32 * D + 4 * half;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -322,25 +357,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         w[1] = (OT)(acc[mt][4 * g + 1] * inv);
         w[2] = (OT)(acc[mt][4 * g + 2] * inv);
         w[3] = (OT)(acc[mt][4 * g + 3] * inv);
-        *(ox4*)(os + mt * 32 + 8 * g + 4 * half) = w;
+        *(ox4*)(orow + (((4 * mt + g) ^ kxor) << 3)) = w;
       }
-  }
-  __syncthreads();
-  if (active) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the staged rows are in LDS
+    __builtin_amdgcn_wave_barrier();
     constexpr int WR = 64 / C::CPR;   // rows per wave pass
     const uint32_t wcol = lane % C::CPR;
     const uint32_t wrow = lane / C::CPR;
     const int32_t oo = (q0 + l32 < L) ? a.mo.row_off(q0 + l32) : -1;
-    const OT* os = (const OT*)ostage + wave * 32 * C::KP;
 #pragma unroll
     for (int i = 0; i < 32 / WR; ++i) {
-      const int r = wrow + i * WR;
+      const uint32_t r = wrow + i * WR;
       const int32_t o = shfl(oo, r);
-      if (o >= 0) {
-        const uint2 lo = *(const uint2*)(os + r * C::KP + wcol * 8);
-        const uint2 hi = *(const uint2*)(os + r * C::KP + wcol * 8 + 4);
-        *(uint4*)(og + o + wcol * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
+      const uint4 x = *(const uint4*)(ostage + r * D + ((wcol ^ (r & (C::CPR - 1))) << 3));
+      if (o >= 0) *(uint4*)(og + o + wcol * 8) = x;
     }
   }
 }
@@ -368,10 +398,16 @@ hipError_t launch_types(const AttnArgs& a, int head_dim, int nw, hipStream_t str
 
 }  // namespace
 
-// Waves per workgroup: 2 for units of at most 64 rows, else 4.
+// Waves per workgroup: 2 for units of at most 64 rows, else 4.  Measured on the
+// high-resolution and 5B-DiT-shaped workloads, 4-wave workgroups (three per CU at
+// this kernel's register and LDS use) beat 3-, 5-, 6- and 8-wave ones even where
+// those leave fewer idle waves on a unit's last query chunk: more independent
+// workgroups per CU hide the per-block barrier and load latency better.
+int pick_waves(uint32_t L) { return L > 64 ? 4 : 2; }
+
 hipError_t launch_attn_bf16(AttnArgs a, int head_dim, VType vtype, hipStream_t stream) {
   const uint32_t tiles = (a.L + 31) / 32;
-  const int nw = tiles > 2 ? 4 : 2;
+  const int nw = pick_waves(a.L);
   a.nchunks = (tiles + nw - 1) / nw;
   switch (vtype) {
     case VType::kBf16ToBf16: return launch_types<__bf16, __bf16>(a, head_dim, nw, stream);
