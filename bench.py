@@ -37,6 +37,7 @@ def parse():
     p.add_argument("--workload", default="highres_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-permutations", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's timed sample")
     return p.parse_args()
 
@@ -192,6 +193,10 @@ def main():
         "source_digest": digest,
     }
 
+    perms = None
+    if not args.no_permutations:
+        perms = permutation_rates(sq, cfg, q, stream)
+
     dense = None
     if not args.no_dense:
         del out, ws
@@ -229,8 +234,35 @@ def main():
         "roofline": roofline,
         "cpu_baseline": base,
         "dense_comparator": dense,
+        "permutations": perms,
     }
     print(json.dumps(line), flush=True)
+
+
+def permutation_rates(sq, cfg, q, stream):
+    """GB/s (read + write bytes / HIP-event time) of the standalone reshaping kernels
+    on the workload's q tensor: tile gather, window-to-group regroup, tile scatter."""
+    import torch
+
+    B, n, H, d, W, G = cfg.batch, cfg.n, cfg.heads, cfg.head_dim, cfg.window, cfg.windows
+    win = torch.empty((B, H, G, W, d), dtype=q.dtype, device=q.device)
+    grp = torch.empty((B, H, W, G, d), dtype=q.dtype, device=q.device)
+    tok = torch.empty_like(q)
+    nbytes = 2.0 * q.numel() * q.element_size()
+    runs = {
+        "tile_gather": lambda: sq.squad_tile_gather(q, cfg.grid, cfg.tile, dst=win, stream=stream),
+        "window_to_group": lambda: sq.squad_window_to_group(win, cfg.grid, cfg.tile, dst=grp, stream=stream),
+        "tile_scatter": lambda: sq.squad_tile_scatter(win, cfg.grid, cfg.tile, dst=tok, stream=stream),
+    }
+    out = {}
+    for name, fn in runs.items():
+        fn()
+        torch.cuda.synchronize()
+        ms = time_launches(fn, stream, 10)
+        out[name] = {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                     "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del win, grp, tok
+    return out
 
 
 def dense_comparator(sq, inputs, dev):
