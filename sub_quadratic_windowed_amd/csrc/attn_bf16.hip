@@ -34,6 +34,12 @@
 // Rows past the end of a unit read the unit's last row (their logits are masked to
 // -inf, so they carry zero weight) and are never stored.
 //
+// Address work: for units of at most TABLE_ROWS rows every row's element offset is
+// formed once per workgroup into an LDS table, so locating a block's rows is one LDS
+// read per load; the direct loads take a uniform base plus a 32-bit byte offset.  The
+// two 32-lane halves of a wave combine their row statistics with one lane-half swap
+// (v_permlane32_swap) rather than an LDS round trip.
+//
 // The softmax keeps a reference maximum that is raised only when a block's maximum
 // exceeds it by more than 2^8 in the exp2 domain; until then the weights are
 // exp2(logit - reference) <= 256, well inside fp16/bf16 range, and the accumulator
@@ -54,6 +60,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BN = 32;              // keys per block
 constexpr float RESCALE_TAU = 8.f;  // log2 headroom before the reference max is raised
+constexpr int TABLE_ROWS = 512;     // units of at most this many rows keep their row offsets in LDS
 
 template <typename T> struct Vec;
 template <> struct Vec<__bf16> {
@@ -91,7 +98,15 @@ __device__ __forceinline__ void wait_newest(int n) {
   }
 }
 
-__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
+// the value of lane l ^ 32, combined with this lane's: one swap of the two 32-lane halves
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ int shfl(int x, int src) { return __shfl(x, src, 64); }
 
 template <int D, int NW>
@@ -123,7 +138,7 @@ struct Stage {
   }
 };
 
-template <int D, int NW, typename VT, typename OT>
+template <int D, int NW, typename VT, typename OT, bool TAB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(AttnArgs a) {
   typedef Cfg<D, NW> C;
   typedef typename Vec<VT>::x8 vx8;
@@ -156,6 +171,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 
   const uint32_t L = a.L;
   const uint32_t nkb = (L + BN - 1) / BN;
+  // units of at most TABLE_ROWS rows: every row's offset is formed once, into LDS
+  __shared__ int32_t ktab[TAB ? TABLE_ROWS : 1];
+  __shared__ int32_t vtab[TAB ? TABLE_ROWS : 1];
+  if constexpr (TAB) {
+    for (uint32_t r = tid; r < L; r += C::NT) {
+      const int32_t ko = a.mqk.row_off(r);
+      ktab[r] = ko;
+      vtab[r] = a.v_like_k ? ko : a.mv.row_off(r);
+    }
+    __syncthreads();
+  }
   const uint32_t q0 = chunk * C::BM + wave * 32;   // first query row of this wave
   const bool active = q0 < L;
 
@@ -194,15 +220,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // address arithmetic stay off the path between a block's barrier and its MFMAs.
   int32_t pk[C::VPW], pv[C::VPW];
   auto prep_block = [&](uint32_t kb) {
-    const int32_t ko = key_offset(a.mqk, kb);
-    const int32_t vo = v_offset(kb, ko);
+    if constexpr (TAB) {
 #pragma unroll
-    for (int i = 0; i < C::VPW; ++i) {
-      const int ins = wave + i * NW;
-      const uint32_t krow = C::KRPI * ins + krow0;
-      const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
-      pk[i] = shfl(ko, krow & 31) + (int32_t)(kchunk * 8);
-      pv[i] = shfl(vo, (4 * C::GPI * ins + vrow0) & 31) + (int32_t)(vcol * 8);
+      for (int i = 0; i < C::VPW; ++i) {
+        const int ins = wave + i * NW;
+        const uint32_t krow = C::KRPI * ins + krow0;
+        const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
+        pk[i] = 2 * (ktab[min(kb * BN + (krow & 31), L - 1)] + (int32_t)(kchunk * 8));
+        pv[i] = 2 * (vtab[min(kb * BN + ((4 * C::GPI * ins + vrow0) & 31), L - 1)] + (int32_t)(vcol * 8));
+      }
+    } else {
+      const int32_t ko = key_offset(a.mqk, kb);
+      const int32_t vo = v_offset(kb, ko);
+#pragma unroll
+      for (int i = 0; i < C::VPW; ++i) {
+        const int ins = wave + i * NW;
+        const uint32_t krow = C::KRPI * ins + krow0;
+        const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
+        pk[i] = 2 * (shfl(ko, krow & 31) + (int32_t)(kchunk * 8));
+        pv[i] = 2 * (shfl(vo, (4 * C::GPI * ins + vrow0) & 31) + (int32_t)(vcol * 8));
+      }
     }
   };
   // the prepared block's K and V rows into stage ST
@@ -214,8 +251,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     for (int i = 0; i < C::VPW; ++i) {
       const int ins = wave + i * NW;
       if (C::VPW * NW != C::VINS && ins >= C::VINS) break;
-      __builtin_amdgcn_global_load_lds((const void*)(kg + pk[i]), (lds_void_t*)(ks + ins * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg + pv[i]), (lds_void_t*)(vs + ins * 512), 16, 0, 0);
+      // uniform base + unsigned 32-bit byte offset: one offset register per load
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)kg + (uint32_t)pk[i]),
+                                       (lds_void_t*)(ks + ins * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)vg + (uint32_t)pv[i]),
+                                       (lds_void_t*)(vs + ins * 512), 16, 0, 0);
     }
   };
 
@@ -234,7 +274,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     issue_block(std::integral_constant<int, 1>{});
   }
   if (nkb > 2) prep_block(2);
-  wait_loads(nkb > 1);
+  wait_vmcnt<0>();   // the query rows and blocks 0 and 1 have landed
   __builtin_amdgcn_s_barrier();
 
   f32x16 acc[D / 32];
@@ -259,7 +299,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   auto step = [&](uint32_t kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const bool has2 = kb + 2 < nkb;
-    if (has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
+    // (the compiler waits for every outstanding load before the first LDS read after
+    // the loop head, so in the loop's first step the loads go out after the scores)
+    if (ST != 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
 
     if (active) {
       const __bf16* ks = Stage<D, ST>::k() + l32 * D;
@@ -274,6 +316,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
       }
+      // the direct loads above read their offset registers after issue: keep those
+      // registers from being reused as destinations of the reads just above
+#pragma unroll
+      for (int i = 0; i < C::VPW; ++i) asm volatile("" ::"v"(pk[i]), "v"(pv[i]));
+      if (ST == 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
       // keys past the end of the unit take no weight
       if ((kb + 1) * BN > L) {
 #pragma unroll
@@ -285,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       float mx = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = fmaxf(mx, xhalf(mx)) * c;
+      mx = max_halves(mx) * c;
       if (kb == 0) {
         m_ref = mx;
       } else if (__any(mx > m_ref + RESCALE_TAU)) {
@@ -328,17 +375,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         }
       }
     }
+    if (ST == 0 && has2 && !active) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
     if (kb + 3 < nkb) prep_block(kb + 3);
     // this wave's loads of block kb + 1 have landed (only block kb + 2 may be in
     // flight); the barrier then publishes them and retires stage ST's readers
     wait_loads(has2);
     __builtin_amdgcn_s_barrier();
   };
-  for (uint32_t kb = 0; kb < nkb; kb += 3) {
+  // whole rounds of three steps, then the remainder: every path through the loop body
+  // is the same, so the compiler can tell which stage's loads are still in flight
+  uint32_t kb = 0;
+  for (; kb + 3 <= nkb; kb += 3) {
     step(kb, std::integral_constant<int, 0>{});
-    if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
-    if (kb + 2 < nkb) step(kb + 2, std::integral_constant<int, 2>{});
+    step(kb + 1, std::integral_constant<int, 1>{});
+    step(kb + 2, std::integral_constant<int, 2>{});
   }
+  if (kb < nkb) step(kb, std::integral_constant<int, 0>{});
+  if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
 
   // ---- epilogue: normalise; each wave stages its 32 rows in a free stage buffer
   // (chunk c of row r at slot c ^ (r % CPR)) and stores them as 16-byte chunks
@@ -346,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
                      : wave == 2 ? Stage<D, 2>::k() : Stage<D, 0>::v());
   if (NW > 4) ostage = nullptr;  // (only 2- and 4-wave workgroups are launched)
   if (active) {
-    const float inv = 1.f / (l_run + xhalf(l_run));
+    const float inv = 1.f / sum_halves(l_run);
     OT* orow = ostage + l32 * D + 4 * half;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
@@ -380,7 +433,10 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const uint32_t groups = (a.units + 7) / 8;
   const uint64_t blocks = (uint64_t)groups * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
+  if (a.L <= TABLE_ROWS)
+    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, false>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
