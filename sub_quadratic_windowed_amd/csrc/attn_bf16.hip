@@ -34,16 +34,20 @@
 // Rows past the end of a unit read the unit's last row (their logits are masked to
 // -inf, so they carry zero weight) and are never stored.
 //
-// Address work: for units of at most TABLE_ROWS rows every row's element offset is
-// formed once per workgroup into an LDS table, so locating a block's rows is one LDS
-// read per load; the direct loads take a uniform base plus a 32-bit byte offset.  The
+// Address work: for units of at most TABLE_ROWS rows every row's byte offset is
+// formed once per workgroup into an LDS table (padded to whole blocks with the last
+// row), so locating a block's rows is one LDS read and one add per load; the direct
+// loads take a uniform base plus a 32-bit byte offset, and the K reads a per-lane
+// offset with the stage's LDS address as the instruction's immediate.  The
 // two 32-lane halves of a wave combine their row statistics with one lane-half swap
 // (v_permlane32_swap) rather than an LDS round trip.
 //
 // The softmax keeps a reference maximum that is raised only when a block's maximum
 // exceeds it by more than 2^8 in the exp2 domain; until then the weights are
 // exp2(logit - reference) <= 256, well inside fp16/bf16 range, and the accumulator
-// needs no rescaling.  The row sum divides it out at the end.
+// needs no rescaling.  The row sum adds the weights as rounded for the products
+// (two per v_dot2 instruction), so the normalised weights of a row sum to one
+// exactly as applied; it divides the accumulator out at the end.
 #include "squad_kernels.h"
 
 namespace squad {
@@ -108,6 +112,34 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ int shfl(int x, int src) { return __shfl(x, src, 64); }
+
+// sum of 16 rounded weights (two 8-element vectors) added to acc, two per instruction
+__device__ __forceinline__ float row_sum(const bf16x8 (&pb)[2], float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 one = {(__bf16)1.f, (__bf16)1.f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const b2 x = {pb[0][2 * e], pb[0][2 * e + 1]};
+    const b2 y = {pb[1][2 * e], pb[1][2 * e + 1]};
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(x, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(y, one, s1, false);
+  }
+  return acc + (s0 + s1);
+}
+__device__ __forceinline__ float row_sum(const f16x8 (&pb)[2], float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(_Float16)1.f, (_Float16)1.f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const h2 x = {pb[0][2 * e], pb[0][2 * e + 1]};
+    const h2 y = {pb[1][2 * e], pb[1][2 * e + 1]};
+    s0 = __builtin_amdgcn_fdot2(x, one, s0, false);
+    s1 = __builtin_amdgcn_fdot2(y, one, s1, false);
+  }
+  return acc + (s0 + s1);
+}
 
 template <int D, int NW>
 struct Cfg {
@@ -175,10 +207,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   __shared__ int32_t ktab[TAB ? TABLE_ROWS : 1];
   __shared__ int32_t vtab[TAB ? TABLE_ROWS : 1];
   if constexpr (TAB) {
-    for (uint32_t r = tid; r < L; r += C::NT) {
-      const int32_t ko = a.mqk.row_off(r);
-      ktab[r] = ko;
-      vtab[r] = a.v_like_k ? ko : a.mv.row_off(r);
+    // byte offsets; rows past the end of the unit (up to a whole block) repeat its last row
+    for (uint32_t r = tid; r < nkb * BN; r += C::NT) {
+      const uint32_t rr = min(r, L - 1);
+      const int32_t ko = a.mqk.row_off(rr);
+      ktab[r] = 2 * ko;
+      vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
     }
     __syncthreads();
   }
@@ -226,8 +260,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         const int ins = wave + i * NW;
         const uint32_t krow = C::KRPI * ins + krow0;
         const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
-        pk[i] = 2 * (ktab[min(kb * BN + (krow & 31), L - 1)] + (int32_t)(kchunk * 8));
-        pv[i] = 2 * (vtab[min(kb * BN + ((4 * C::GPI * ins + vrow0) & 31), L - 1)] + (int32_t)(vcol * 8));
+        pk[i] = ktab[kb * BN + (krow & 31)] + (int32_t)(kchunk * 16);
+        pv[i] = vtab[kb * BN + ((4 * C::GPI * ins + vrow0) & 31)] + (int32_t)(vcol * 16);
       }
     } else {
       const int32_t ko = key_offset(a.mqk, kb);
@@ -294,6 +328,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // the A operand of the scores: row l32, logical chunk 2 kk + half, stored at
   // slot (2 kk + half) ^ (l32 % CPR)
   const uint32_t kxor = l32 & (C::CPR - 1);
+  // byte offset of this lane's K chunk 2 kk + half in any stage (row l32, swizzled slot)
+  uint32_t kofs[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kofs[kk] = l32 * D * 2 + ((((uint32_t)(2 * kk) + half) ^ kxor) << 4);
 
   // one key block held in stage ST; requests block kb + 2 into stage (ST + 2) % 3
   auto step = [&](uint32_t kb, auto st_tag) {
@@ -304,15 +342,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     if (ST != 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
 
     if (active) {
-      const __bf16* ks = Stage<D, ST>::k() + l32 * D;
+      const char* ks = (const char*)Stage<D, ST>::k();
       f32x16 sc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const __bf16* kp = ks + (((2 * kk + half) ^ kxor) << 3);
+        const char* kp = ks + kofs[kk];
         const uint2 lo = *(const uint2*)kp;
-        const uint2 hi = *(const uint2*)(kp + 4);
+        const uint2 hi = *(const uint2*)(kp + 8);
         const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
       }
@@ -345,15 +383,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mt][r] *= alpha;
       }
-      float ps = 0.f;
       vx8 pb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -m_ref));
-        ps += p;
-        pb[r / 8][r % 8] = (VT)p;
-      }
-      l_run += ps;
+      for (int r = 0; r < 16; ++r) pb[r / 8][r % 8] = (VT)__builtin_amdgcn_exp2f(fmaf(sc[r], c, -m_ref));
+      // the row sum adds the rounded weights the products use, two per instruction
+      l_run = row_sum(pb, l_run);
       // O^T += V^T P^T, 16 keys per MFMA
       const VT* vs = (const VT*)Stage<D, ST>::v() + toff;
 #pragma unroll
