@@ -82,6 +82,60 @@ def test_forward_matches_oracle(case):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("scale", [0.3, 1e-3], ids=["scale0.3", "scale1e-3"])
+def test_forward_custom_scale(dtype, scale):
+    """A caller-given softmax scale reaches both passes (1e-3 makes both passes
+    nearly uniform averages)."""
+    grid, tile = (4, 6, 10), (2, 3, 5)
+    q, k, v = rand_inputs((1, 240, 2, 128), dtype, 11)
+    out = sq.squad_attn_forward(q, k, v, grid, tile, 2, scale=scale)
+    torch.cuda.synchronize()
+    want = oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile, scale=scale)
+    assert maxerr(out, want) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_forward_window_beyond_row_tables(dtype):
+    """W = 576 rows per window: the local pass locates rows without the per-unit
+    LDS tables (more than 512 rows), the global pass has G = 2 rows per group."""
+    grid, tile = (4, 12, 24), (4, 12, 12)
+    q, k, v = rand_inputs((1, 1152, 2, 128), dtype, 12)
+    out = sq.squad_attn_forward(q, k, v, grid, tile, 2)
+    torch.cuda.synchronize()
+    want = oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)
+    assert maxerr(out, want) <= TOL[dtype]
+
+
+def test_forward_sharp_attention_rescales():
+    """q and k scaled by 4: logits with a standard deviation near 16, so the running
+    maximum is raised (and the accumulator rescaled) in the middle of units."""
+    grid, tile = (4, 16, 20), (4, 8, 10)
+    q, k, v = rand_inputs((1, 1280, 2, 128), torch.bfloat16, 13)
+    q, k = q * 4, k * 4   # exact in bf16 (a power of two)
+    out = sq.squad_attn_forward(q, k, v, grid, tile, 2)
+    torch.cuda.synchronize()
+    want = oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)
+    assert np.isfinite(f64(out)).all()
+    assert maxerr(out, want) <= TOL[torch.bfloat16]
+
+
+def test_forward_reuses_buffers():
+    """Two calls with the same preallocated output and workspace, the second on other
+    inputs, each match the oracle (nothing from the first call leaks into the second)."""
+    grid, tile = (4, 6, 10), (2, 3, 5)
+    shape = (1, 240, 3, 128)
+    ws = torch.empty(sq.squad_attn_workspace_size(grid, tile, 3, 1, 128, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    for seed in (14, 15):
+        q, k, v = rand_inputs(shape, torch.bfloat16, seed, peaky=True)
+        sq.squad_attn_forward(q, k, v, grid, tile, 3, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        want = oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)
+        assert maxerr(out, want) <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("case", FORWARD_CASES[:8], ids=lambda c: f"{c[0]}-{c[1]}-{str(c[5])[6:]}")
 def test_each_pass_matches_oracle(case):
     grid, tile, B, Hh, d, dtype, peaky = case
