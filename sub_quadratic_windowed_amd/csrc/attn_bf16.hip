@@ -203,6 +203,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 
   const uint32_t L = a.L;
   const uint32_t nkb = (L + BN - 1) / BN;
+  const uint32_t q0 = chunk * C::BM + wave * 32;   // first query row of this wave
+  const bool active = q0 < L;
+
+  // ---- prologue: the query rows go straight into the B-operand registers first, so
+  // their latency overlaps the row tables
+  bf16x8 qf[D / 16];
+  {
+    const uint32_t qrow = min(q0 + l32, L - 1);
+    const __bf16* qr = qg + a.mqk.row_off(qrow) + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
+  }
   // units of at most TABLE_ROWS rows: every row's offset is formed once, into LDS
   __shared__ int32_t ktab[TAB ? TABLE_ROWS : 1];
   __shared__ int32_t vtab[TAB ? TABLE_ROWS : 1];
@@ -214,10 +226,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       ktab[r] = 2 * ko;
       vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
     }
-    __syncthreads();
+    // the table writes have completed; the barrier publishes them (no vmcnt wait:
+    // the query rows may still be in flight)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
   }
-  const uint32_t q0 = chunk * C::BM + wave * 32;   // first query row of this wave
-  const bool active = q0 < L;
 
   // lane l (< 32) locates key l of a block; lanes 32-63 mirror lanes 0-31
   auto key_offset = [&](const RowMap& m, uint32_t kb) -> int32_t {
@@ -293,14 +306,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
   };
 
-  // ---- prologue: Q registers; blocks 0 and 1 requested
-  bf16x8 qf[D / 16];
-  {
-    const uint32_t qrow = min(q0 + l32, L - 1);
-    const __bf16* qr = qg + a.mqk.row_off(qrow) + half * 8;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
-  }
+  // blocks 0 and 1 requested
   prep_block(0);
   issue_block(std::integral_constant<int, 0>{});
   if (nkb > 1) {
@@ -333,10 +339,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) kofs[kk] = l32 * D * 2 + ((((uint32_t)(2 * kk) + half) ^ kxor) << 4);
 
-  // one key block held in stage ST; requests block kb + 2 into stage (ST + 2) % 3
-  auto step = [&](uint32_t kb, auto st_tag) {
+  // one key block held in stage ST; requests block kb + 2 into stage (ST + 2) % 3.
+  // ALL: blocks kb + 2 and kb + 3 exist (known at compile time, so the steps of the
+  // main loop have no conditional loads and the compiler's waits stay exact)
+  auto step = [&](uint32_t kb, auto st_tag, auto all_tag) {
     constexpr int ST = decltype(st_tag)::value;
-    const bool has2 = kb + 2 < nkb;
+    constexpr bool ALL = decltype(all_tag)::value;
+    const bool has2 = ALL || kb + 2 < nkb;
     // (the compiler waits for every outstanding load before the first LDS read after
     // the loop head, so in the loop's first step the loads go out after the scores)
     if (ST != 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
@@ -410,22 +419,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       }
     }
     if (ST == 0 && has2 && !active) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
-    if (kb + 3 < nkb) prep_block(kb + 3);
+    if (ALL || kb + 3 < nkb) prep_block(kb + 3);
     // this wave's loads of block kb + 1 have landed (only block kb + 2 may be in
     // flight); the barrier then publishes them and retires stage ST's readers
     wait_loads(has2);
     __builtin_amdgcn_s_barrier();
   };
-  // whole rounds of three steps, then the remainder: every path through the loop body
-  // is the same, so the compiler can tell which stage's loads are still in flight
+  // whole rounds of three steps (first those whose blocks all have successors to
+  // request, then the last rounds), then the remainder: every path through a loop
+  // body is the same, so the compiler can tell which stage's loads are in flight
   uint32_t kb = 0;
-  for (; kb + 3 <= nkb; kb += 3) {
-    step(kb, std::integral_constant<int, 0>{});
-    step(kb + 1, std::integral_constant<int, 1>{});
-    step(kb + 2, std::integral_constant<int, 2>{});
+  for (; kb + 6 <= nkb; kb += 3) {
+    step(kb, std::integral_constant<int, 0>{}, std::true_type{});
+    step(kb + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    step(kb + 2, std::integral_constant<int, 2>{}, std::true_type{});
   }
-  if (kb < nkb) step(kb, std::integral_constant<int, 0>{});
-  if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{});
+  for (; kb + 3 <= nkb; kb += 3) {
+    step(kb, std::integral_constant<int, 0>{}, std::false_type{});
+    step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    step(kb + 2, std::integral_constant<int, 2>{}, std::false_type{});
+  }
+  if (kb < nkb) step(kb, std::integral_constant<int, 0>{}, std::false_type{});
+  if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
 
   // ---- epilogue: normalise; each wave stages its 32 rows in a free stage buffer
   // (chunk c of row r at slot c ^ (r % CPR)) and stores them as 16-byte chunks
