@@ -249,7 +249,10 @@ def test_highres_properties():
 
 # ---------------------------------------------------------------- the engine and the comparator
 
-@pytest.mark.parametrize("L", [1, 17, 64, 100, 160, 480, 512, 600])
+# L spans every shape of the block loop: 1-2 blocks (2-wave workgroups), 3-5 blocks (no
+# round with all successors), 6-9 blocks (one such round, then the last round and a
+# remainder of 0-2 blocks), 15-16 blocks (the full-size units) and beyond the row tables
+@pytest.mark.parametrize("L", [1, 17, 64, 65, 96, 100, 160, 192, 200, 256, 288, 384, 480, 512, 600])
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
 def test_window_attn_matches_oracle(L, dtype, d):
     U = 40
