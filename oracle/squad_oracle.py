@@ -25,11 +25,17 @@ Readings taken where the pages are silent (each one is also listed in the design
 notes of this repository):
 
 * Tokens are the cells of a T x H x W latent grid, flattened row-major over
-  (t, h, w).  A window is a tt x th x tw tile of that grid; the grid must be a
-  whole number of tiles.  Windows are numbered row-major over the window grid
-  (T/tt, H/th, W/tw); the relative position (offset) of a token inside its window
-  is numbered row-major over (tt, th, tw).  Only the partitions matter: attention
-  is permutation-equivariant inside a window and inside an offset group.
+  (t, h, w).  A window is a tt x th x tw tile of that grid.  Windows are numbered
+  row-major over the window grid (ceil(T/tt), ceil(H/th), ceil(W/tw)); the
+  relative position (offset) of a token inside its window is numbered row-major
+  over (tt, th, tw).  Only the partitions matter: attention is
+  permutation-equivariant inside a window and inside an offset group.
+* A grid that is not a whole number of tiles is read as padded up to one with
+  absent tokens: the tiles along the far edges are cut by the grid, so their
+  windows hold fewer tokens, and an offset group holds one token per window that
+  has a token at that offset.  Absent tokens are neither keys nor queries (the
+  pages only use whole tiles; this is the plainest extension, and on a whole
+  number of tiles it is the operator above).
 * The global pass uses the same q and k as the local pass (there are no extra
   parameters), with v replaced by the local output; out = Attn_G(q, k, Attn_L(q, k, v)).
   Nothing is added to it (no residual, gate or sum).
@@ -46,6 +52,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "is_whole",
+    "padded_window_index",
     "window_index",
     "softmax_attention",
     "local_pass",
@@ -60,14 +68,37 @@ __all__ = [
 ]
 
 
-def _check_grid(grid, tile):
+def _check_grid(grid, tile, partial=False):
     T, H, W = (int(x) for x in grid)
     tt, th, tw = (int(x) for x in tile)
     if min(T, H, W, tt, th, tw) <= 0:
         raise ValueError("grid and tile sizes must be positive")
-    if T % tt or H % th or W % tw:
+    if tt > T or th > H or tw > W:
+        raise ValueError(f"tile {tile} is larger than grid {grid}")
+    if not partial and (T % tt or H % th or W % tw):
         raise ValueError(f"grid {grid} is not a whole number of {tile} tiles")
     return T, H, W, tt, th, tw
+
+
+def is_whole(grid, tile) -> bool:
+    """True when the grid is a whole number of tiles."""
+    return all(int(x) % int(y) == 0 for x, y in zip(grid, tile))
+
+
+def padded_window_index(grid, tile) -> np.ndarray:
+    """Token index of every (window, offset) pair of a possibly cut tiling.
+
+    idx[g, p] is the token at offset p of window g, or -1 where the tile reaches
+    past the grid; windows run row-major over (ceil(T/tt), ceil(H/th), ceil(W/tw)).
+    On a whole number of tiles this equals window_index.
+    """
+    T, H, W, tt, th, tw = _check_grid(grid, tile, partial=True)
+    nt, nh, nw = -(-T // tt), -(-H // th), -(-W // tw)
+    gt, gh, gw, at, ah, aw = np.ix_(np.arange(nt), np.arange(nh), np.arange(nw),
+                                    np.arange(tt), np.arange(th), np.arange(tw))
+    t, h, w = gt * tt + at, gh * th + ah, gw * tw + aw
+    idx = np.where((t < T) & (h < H) & (w < W), (t * H + h) * W + w, -1)
+    return idx.reshape(nt * nh * nw, tt * th * tw)
 
 
 def window_index(grid, tile) -> np.ndarray:
@@ -124,8 +155,10 @@ def local_pass(q, k, v, grid, tile, scale=None) -> np.ndarray:
     gist.science technical summary, "1. SQuad-Attention Operator", Local Pass.
     """
     q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
-    idx = window_index(grid, tile)                      # [G, Wn]
     s = _default_scale(q.shape[-1], scale)
+    if not is_whole(grid, tile):
+        return _unit_attention(q, k, v, padded_window_index(grid, tile), s)
+    idx = window_index(grid, tile)                      # [G, Wn]
     # [B, G, Wn, Hh, d] -> [B, Hh, G, Wn, d]
     qw = q[:, idx].transpose(0, 3, 1, 2, 4)
     kw = k[:, idx].transpose(0, 3, 1, 2, 4)
@@ -143,14 +176,32 @@ def global_pass(q, k, v, grid, tile, scale=None) -> np.ndarray:
     Here v is the value stream, which in the operator is the local pass's output.
     """
     q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
-    grp = window_index(grid, tile).T                    # [Wn, G]: group p = tokens at offset p
     s = _default_scale(q.shape[-1], scale)
+    if not is_whole(grid, tile):
+        return _unit_attention(q, k, v, padded_window_index(grid, tile).T, s)
+    grp = window_index(grid, tile).T                    # [Wn, G]: group p = tokens at offset p
     qg = q[:, grp].transpose(0, 3, 1, 2, 4)             # [B, Hh, Wn, G, d]
     kg = k[:, grp].transpose(0, 3, 1, 2, 4)
     vg = v[:, grp].transpose(0, 3, 1, 2, 4)
     og = softmax_attention(qg, kg, vg, s)
     o = np.empty_like(v)
     o[:, grp] = og.transpose(0, 2, 3, 1, 4)
+    return o
+
+
+def _unit_attention(q, k, v, units, s) -> np.ndarray:
+    """Softmax attention inside each unit (a row of `units`, -1 = absent token).
+
+    Every token of the grid belongs to exactly one unit; each unit is attended
+    on its own, over its present tokens only.
+    """
+    o = np.empty_like(v)
+    for row in units:
+        tok = row[row >= 0]
+        qu = q[:, tok].transpose(0, 2, 1, 3)            # [B, Hh, L, d]
+        ku = k[:, tok].transpose(0, 2, 1, 3)
+        vu = v[:, tok].transpose(0, 2, 1, 3)
+        o[:, tok] = softmax_attention(qu, ku, vu, s).transpose(0, 2, 1, 3)
     return o
 
 

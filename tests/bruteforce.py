@@ -26,7 +26,9 @@ def window_id(grid, tile):
     T, H, W = grid
     tt, th, tw = tile
     t, h, w = coords(grid)
-    return ((t // tt) * (H // th) + h // th) * (W // tw) + w // tw
+    # windows of a cut tiling (grid not a whole number of tiles) keep the
+    # ceil-sized window grid; absent tokens simply do not occur
+    return ((t // tt) * (-(-H // th)) + h // th) * (-(-W // tw)) + w // tw
 
 
 def offset_id(grid, tile):

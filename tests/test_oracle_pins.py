@@ -263,3 +263,93 @@ def test_window_attn_rows_are_convex_combinations():
     o = oracle.window_attn(q, k, v)
     assert np.all(o <= v.max(1, keepdims=True) + 1e-12) and np.all(o >= v.min(1, keepdims=True) - 1e-12)
     np.testing.assert_allclose(o, sdpa64(q[:, :, None], k[:, :, None], v[:, :, None], 0.25)[:, :, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------- tilings cut by the grid edge
+
+# (grid, tile) pairs whose grid is not a whole number of tiles: cuts along one, two
+# and three axes, a tile as large as the grid along an axis, single-token edge windows
+CUT_SHAPES = [
+    ((3, 5, 7), (2, 2, 3)),
+    ((4, 6, 5), (3, 4, 2)),
+    ((5, 5, 5), (2, 3, 4)),
+    ((2, 4, 7), (2, 4, 3)),   # cut along w only
+    ((3, 3, 3), (2, 2, 2)),   # the corner window holds one token
+    ((1, 5, 6), (1, 5, 4)),
+]
+
+
+@pytest.mark.parametrize("grid,tile", CUT_SHAPES)
+def test_padded_window_index_is_the_cut_partition(grid, tile):
+    idx = oracle.padded_window_index(grid, tile)
+    n = int(np.prod(grid))
+    present = idx[idx >= 0]
+    assert np.array_equal(np.sort(present), np.arange(n))              # every token once
+    wid, off = bf.window_id(grid, tile), bf.offset_id(grid, tile)
+    G, Wn = idx.shape
+    assert Wn == int(np.prod(tile))
+    for g in range(G):
+        row = idx[g][idx[g] >= 0]
+        assert row.size > 0 and np.all(wid[row] == g)
+        # a window holds the tile's box clipped by the grid: the product of the clipped extents
+        t0 = (g // (-(-grid[1] // tile[1]) * -(-grid[2] // tile[2]))) * tile[0]
+        h0 = (g // -(-grid[2] // tile[2])) % -(-grid[1] // tile[1]) * tile[1]
+        w0 = g % -(-grid[2] // tile[2]) * tile[2]
+        ext = [min(tile[0], grid[0] - t0), min(tile[1], grid[1] - h0), min(tile[2], grid[2] - w0)]
+        assert row.size == int(np.prod(ext))
+    for p in range(Wn):
+        col = idx[:, p][idx[:, p] >= 0]
+        assert np.all(off[col] == p)
+
+
+@pytest.mark.parametrize("grid,tile", SHAPES)
+def test_padded_window_index_on_whole_tilings(grid, tile):
+    assert np.array_equal(oracle.padded_window_index(grid, tile), oracle.window_index(grid, tile))
+
+
+@pytest.mark.parametrize("grid,tile", CUT_SHAPES)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cut_tiling_matches_masked_dense_bruteforce(grid, tile, seed):
+    B, Hh, d = 2, 2, 8
+    q, k, v = rand_qkv(grid, B, Hh, d, seed, "peaky" if seed == 2 else "normal")
+    s = 0.41
+    ref, ref_o1 = bf.squad_bruteforce(q, k, v, grid, tile, s)
+    np.testing.assert_allclose(oracle.local_pass(q, k, v, grid, tile, s), ref_o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.squad_forward(q, k, v, grid, tile, s), ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,tile", SHAPES[:4])
+def test_per_unit_path_equals_batched_path_on_whole_tilings(grid, tile):
+    """The per-unit path that serves cut tilings, run on a whole tiling, gives the
+    batched path's result (the same operator, computed unit by unit)."""
+    q, k, v = rand_qkv(grid, 1, 2, 8, 5)
+    idx = oracle.padded_window_index(grid, tile)
+    s = 0.5
+    np.testing.assert_allclose(oracle.squad_oracle._unit_attention(q, k, v, idx, s),
+                               oracle.local_pass(q, k, v, grid, tile, s), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.squad_oracle._unit_attention(q, k, v, idx.T, s),
+                               oracle.global_pass(q, k, v, grid, tile, s), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,tile", CUT_SHAPES)
+def test_cut_tiling_zero_queries_closed_form(grid, tile):
+    """q = 0: the local output is the mean of v over the token's (clipped) window,
+    and the output is the plain mean, over the windows present in the token's
+    offset group, of those window means; computed here from coordinates."""
+    q, _, v = rand_qkv(grid, 1, 1, 4, 7)
+    q = np.zeros_like(q)
+    k = np.random.default_rng(8).standard_normal(q.shape)
+    out = oracle.squad_forward(q, k, v, grid, tile, 0.9)
+    wid, off = bf.window_id(grid, tile), bf.offset_id(grid, tile)
+    wmean = {g: v[0, wid == g, 0].mean(axis=0) for g in np.unique(wid)}
+    for i in range(int(np.prod(grid))):
+        members = np.flatnonzero(off == off[i])                # the group of token i
+        expect = np.mean([wmean[wid[j]] for j in members], axis=0)
+        np.testing.assert_allclose(out[0, i, 0], expect, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,tile", CUT_SHAPES[:3])
+def test_cut_tiling_constant_values(grid, tile):
+    q, k, _ = rand_qkv(grid, 1, 2, 4, 3)
+    v = np.full_like(q, -1.25)
+    np.testing.assert_allclose(oracle.squad_forward(q, k, v, grid, tile), v, rtol=0, atol=1e-12)
