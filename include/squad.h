@@ -21,6 +21,18 @@
  * Windows are numbered row-major over the window grid (T/tt, H/th, W/tw) and the
  * offset of a token inside its window row-major over (tt, th, tw).
  *
+ * Cut tilings (squad_attn_forward, its two halves, squad_local_pass and
+ * squad_global_pass): a grid that is not a
+ * whole number of tiles (each tile no larger than the grid) is read as padded up to
+ * one with absent tokens.  The window grid is (ceil(T/tt), ceil(H/th), ceil(W/tw));
+ * the tiles on the far edges are cut by the grid, so their windows hold fewer
+ * tokens and an offset group holds one token per window that has that offset.
+ * Absent tokens are neither keys nor queries.  (The pages use whole tiles only;
+ * this is the plainest extension, and on whole tiles it is the operator above.)
+ * In bf16 such calls need G and Wn of at most 512; the permutation entry points
+ * return SQUAD_ERR_SHAPE for cut tilings.  Outputs in token order cover exactly
+ * the n present tokens.
+ *
  * Token-order tensors are contiguous [batch, n, heads, head_dim] (= [B, n, hidden]).
  * Window-major tensors are contiguous [batch, heads, G, Wn, head_dim]; group-major
  * tensors are contiguous [batch, heads, Wn, G, head_dim].
@@ -57,8 +69,10 @@ typedef struct ihipStream_t* squad_stream_t; /* the same type as hipStream_t */
 enum squad_status {
   SQUAD_OK = 0,
   SQUAD_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, unknown selector          */
-  SQUAD_ERR_SHAPE = 2,       /* grid not a whole number of tiles, sizes too large    */
-  SQUAD_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, or dtype unknown                */
+  SQUAD_ERR_SHAPE = 2,       /* tile larger than the grid, a cut tiling where only
+                                whole tilings are accepted, or sizes too large       */
+  SQUAD_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, dtype unknown, or a bf16 cut
+                                tiling with more than 512 windows or tile cells      */
   SQUAD_ERR_ALIAS = 4,       /* an output overlaps an input or the workspace         */
   SQUAD_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned                */
   SQUAD_ERR_WORKSPACE = 6,   /* workspace null or smaller than required             */
@@ -76,7 +90,9 @@ const char* squad_status_string(int status);
  *   q, k, v, out : token order [batch, n, heads, head_dim], dtype `dtype`.
  *   workspace    : device scratch of at least squad_attn_workspace_size(...) bytes;
  *                  holds the local output, group-major [batch, heads, Wn, G,
- *                  head_dim] (fp16 for bf16 calls, fp32 for fp32 calls).
+ *                  head_dim] (fp16 for bf16 calls, fp32 for fp32 calls); on cut
+ *                  tilings G counts every window of the rounded-up window grid and
+ *                  the rows of absent tokens are left unwritten.
  * Enqueues two kernels on `stream`: squad_attn_forward_local, then
  * squad_attn_forward_global.
  */
@@ -106,10 +122,24 @@ int squad_attn_forward_global(const void* q, const void* k,
                               float scale, const void* workspace, size_t workspace_bytes,
                               squad_stream_t stream);
 
-/* Bytes of workspace squad_attn_forward needs (batch*heads*n*head_dim elements of
- * `dtype`); 0 if the arguments are invalid. */
+/* Bytes of workspace squad_attn_forward needs (batch*heads*G*Wn*head_dim elements of
+ * `dtype`, = batch*heads*n*head_dim on whole tilings); 0 if the arguments are
+ * invalid. */
 size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
                                  int32_t batch, int32_t head_dim, int32_t dtype);
+
+/*
+ * Tile planner.  The pages choose windows of about sqrt(n) tokens (technical
+ * summary, "1. SQuad-Attention Operator", Complexiteit: w = sqrt(n) gives
+ * O(n sqrt n)).  On a 3-D grid this picks the tile (tt <= T, th <= H, tw <= W)
+ * that minimises the forward's product work, proportional to
+ * Gp * Wn * (Wn + Gp) with Wn = tt*th*tw and Gp the number of windows of the
+ * (possibly cut) tiling; ties go to the tiling with fewer absent tokens, then to
+ * the smaller tile in (tt, th, tw) order.  Host-only; writes tile_out[3].
+ * Returns SQUAD_ERR_INVALID_ARG for null pointers or sizes <= 0, SQUAD_ERR_SHAPE
+ * for grids of 2^31 tokens or more.
+ */
+int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]);
 
 /*
  * Local pass alone (Attn_L): o1 = softmax attention inside each window.
@@ -178,7 +208,9 @@ int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* 
  *   which = 1: global-pass rows in token order  (units = Wn offsets, rows = G windows)
  *   which = 2: local output in the group-major workspace (units = G, rows = Wn)
  *   which = 3: global-pass value rows in the workspace   (units = Wn, rows = G)
- * offsets must hold batch*heads*n entries.
+ * offsets must hold batch*heads*G*Wn entries (= batch*heads*n on whole tilings).
+ * On a cut tiling, absent rows of the two token maps read -1 (the test the
+ * kernels use to skip them).
  */
 int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t tile[3],
                             int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets);

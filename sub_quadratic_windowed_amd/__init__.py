@@ -20,6 +20,7 @@ __all__ = [
     "SquadError",
     "squad_attn_forward",
     "squad_attn_workspace_size",
+    "squad_plan_tile",
     "squad_attn_forward_local",
     "squad_attn_forward_global",
     "squad_local_pass",
@@ -109,6 +110,14 @@ def squad_attn_workspace_size(grid, tile, heads, batch, head_dim, dtype):
     code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(_lib.lib().squad_attn_workspace_size(_lib.int3(grid), _lib.int3(tile), int(heads),
                                                     int(batch), int(head_dim), code))
+
+
+def squad_plan_tile(grid):
+    """The tile (tt, th, tw) the library's planner picks for a T x H x W grid: the
+    least product work over whole and cut tilings (host-only, no device needed)."""
+    out = (ctypes.c_int32 * 3)()
+    _check(_lib.lib().squad_plan_tile(_lib.int3(grid), out), "squad_plan_tile")
+    return tuple(int(x) for x in out)
 
 
 def squad_attn_forward(q, k, v, grid, tile, heads=None, out=None, scale=None, workspace=None,
@@ -256,8 +265,10 @@ def squad_debug_row_offsets(which, grid, tile, heads, batch, head_dim):
     """Host-side element offsets the kernels use (see include/squad.h); numpy int64."""
     import numpy as np
 
-    n = int(grid[0]) * int(grid[1]) * int(grid[2])
-    out = np.zeros(int(batch) * int(heads) * n, dtype=np.int64)
+    cells = 1   # G * Wn: tile cells of the (possibly cut) tiling, absent ones included
+    for g, t in zip(grid, tile):
+        cells *= -(-int(g) // int(t)) * int(t) if int(t) > 0 else 0
+    out = np.zeros(int(batch) * int(heads) * max(cells, 1), dtype=np.int64)
     st = _lib.lib().squad_debug_row_offsets(int(which), _lib.int3(grid), _lib.int3(tile), int(heads),
                                             int(batch), int(head_dim),
                                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))

@@ -22,6 +22,7 @@ EXPORTS = [
     "squad_status_string",
     "squad_attn_forward",
     "squad_attn_workspace_size",
+    "squad_plan_tile",
     "squad_attn_forward_local",
     "squad_attn_forward_global",
     "squad_local_pass",
@@ -54,6 +55,8 @@ def _declare(lib):
     lib.squad_attn_forward_global.restype = ctypes.c_int
     lib.squad_attn_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32]
     lib.squad_attn_workspace_size.restype = SZ
+    lib.squad_plan_tile.argtypes = [I3, I3]
+    lib.squad_plan_tile.restype = ctypes.c_int
     for name in ("squad_local_pass", "squad_global_pass"):
         f = getattr(lib, name)
         f.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, P]

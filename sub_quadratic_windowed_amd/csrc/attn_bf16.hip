@@ -170,8 +170,11 @@ struct Stage {
   }
 };
 
-template <int D, int NW, typename VT, typename OT, bool TAB>
+// CUT: the grid is not a whole number of tiles; absent rows (the far edges' cut
+// tiles) are neither keys nor stored queries (row tables only, TAB).
+template <int D, int NW, typename VT, typename OT, bool TAB, bool CUT = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(AttnArgs a) {
+  static_assert(TAB || !CUT, "cut tilings use the row tables");
   typedef Cfg<D, NW> C;
   typedef typename Vec<VT>::x8 vx8;
   typedef typename Vec<VT>::x4 vx4;
@@ -205,12 +208,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   const uint32_t nkb = (L + BN - 1) / BN;
   const uint32_t q0 = chunk * C::BM + wave * 32;   // first query row of this wave
   const bool active = q0 < L;
+  UnitDigits ud;
+  if constexpr (CUT) ud = cut_unit_digits(a, s);
+  // row r of the unit is a token (r < L; on cut tilings also inside the grid).
+  // Row 0 always is: the origin of a window, or offset p of the first window.
+  auto present = [&](uint32_t r) -> bool {
+    if constexpr (CUT) return r < L && cut_present(a, ud, r);
+    return r < L;
+  };
 
   // ---- prologue: the query rows go straight into the B-operand registers first, so
   // their latency overlaps the row tables
   bf16x8 qf[D / 16];
   {
-    const uint32_t qrow = min(q0 + l32, L - 1);
+    const uint32_t qrow = CUT ? (present(q0 + l32) ? q0 + l32 : 0) : min(q0 + l32, L - 1);
     const __bf16* qr = qg + a.mqk.row_off(qrow) + half * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
@@ -218,7 +229,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // units of at most TABLE_ROWS rows: every row's offset is formed once, into LDS
   __shared__ int32_t ktab[TAB ? TABLE_ROWS : 1];
   __shared__ int32_t vtab[TAB ? TABLE_ROWS : 1];
-  if constexpr (TAB) {
+  // cut tilings: bit r % 32 of word r / 32 says whether row r is present
+  __shared__ uint32_t rmask[CUT ? TABLE_ROWS / 32 : 1];
+  if constexpr (CUT) {
+    // byte offsets; absent rows (and rows past the end, up to a whole block) read row 0
+    const uint32_t iters = (nkb * BN + C::NT - 1) / C::NT;
+    for (uint32_t i = 0; i < iters; ++i) {
+      const uint32_t r = i * C::NT + tid;
+      const bool ok = r < nkb * BN && present(r);
+      const uint32_t rr = ok ? r : 0;
+      const int32_t ko = a.mqk.row_off(rr);
+      if (r < nkb * BN) {
+        ktab[r] = 2 * ko;
+        vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
+      }
+      const uint64_t bits = __ballot(ok);
+      const uint32_t w0 = (i * C::NT + 64 * wave) / 32;
+      if (lane == 0 && w0 < TABLE_ROWS / 32) {
+        rmask[w0] = (uint32_t)bits;
+        if (w0 + 1 < TABLE_ROWS / 32) rmask[w0 + 1] = (uint32_t)(bits >> 32);
+      }
+    }
+  } else if constexpr (TAB) {
     // byte offsets; rows past the end of the unit (up to a whole block) repeat its last row
     for (uint32_t r = tid; r < nkb * BN; r += C::NT) {
       const uint32_t rr = min(r, L - 1);
@@ -226,6 +258,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       ktab[r] = 2 * ko;
       vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
     }
+  }
+  if constexpr (TAB) {
     // the table writes have completed; the barrier publishes them (no vmcnt wait:
     // the query rows may still be in flight)
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -369,7 +403,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       for (int i = 0; i < C::VPW; ++i) asm volatile("" ::"v"(pk[i]), "v"(pv[i]));
       if (ST == 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
       // keys past the end of the unit take no weight
-      if ((kb + 1) * BN > L) {
+      if constexpr (CUT) {
+        const uint32_t km = rmask[kb];
+        if (km != 0xffffffffu) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((km >> (8 * (r / 4) + 4 * half + (r % 4))) & 1)) sc[r] = -INFINITY;
+        }
+      } else if ((kb + 1) * BN > L) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t key = kb * BN + 8 * (r / 4) + 4 * half + (r % 4);
@@ -466,7 +507,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     constexpr int WR = 64 / C::CPR;   // rows per wave pass
     const uint32_t wcol = lane % C::CPR;
     const uint32_t wrow = lane / C::CPR;
-    const int32_t oo = (q0 + l32 < L) ? a.mo.row_off(q0 + l32) : -1;
+    bool qok = q0 + l32 < L;
+    if constexpr (CUT) qok = qok && ((rmask[(q0 + l32) >> 5] >> ((q0 + l32) & 31)) & 1);
+    const int32_t oo = qok ? a.mo.row_off(q0 + l32) : -1;
 #pragma unroll
     for (int i = 0; i < 32 / WR; ++i) {
       const uint32_t r = wrow + i * WR;
@@ -482,7 +525,11 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const uint32_t groups = (a.units + 7) / 8;
   const uint64_t blocks = (uint64_t)groups * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (a.L <= TABLE_ROWS)
+  if (a.cut.on) {
+    // (the host allows cut tilings only where both passes use the row tables)
+    if (a.L > TABLE_ROWS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
+  } else if (a.L <= TABLE_ROWS)
     hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
   else
     hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, false>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);

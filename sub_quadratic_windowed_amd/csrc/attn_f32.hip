@@ -15,7 +15,9 @@ namespace {
 constexpr int KB = 32;   // keys per LDS block
 constexpr int QPB = 64;  // queries per workgroup
 
-template <int D>
+// CUT: the grid is not a whole number of tiles; absent rows are neither keys nor
+// stored queries.
+template <int D, bool CUT>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int DL = D / 4;        // dimensions per lane
   constexpr int CPR = D / 4;       // 16-byte chunks per row (4 floats each)
@@ -25,6 +27,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
   __shared__ __attribute__((aligned(16))) float ks[KB * D];
   __shared__ __attribute__((aligned(16))) float vs[KB * D];
+  __shared__ uint32_t kmask;   // present keys of the current block
 
   const uint32_t tid = threadIdx.x;
   const uint32_t wg = blockIdx.x;
@@ -44,9 +47,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   float* og = (float*)a.o + a.mo.base(b, h, s);
 
   const uint32_t L = a.L;
+  UnitDigits ud;
+  if constexpr (CUT) ud = cut_unit_digits(a, s);
+  auto present = [&](uint32_t r) -> bool {
+    if constexpr (CUT) return r < L && cut_present(a, ud, r);
+    return r < L;
+  };
   const uint32_t qi = chunk * QPB + (tid >> 2);   // this lane's query row
   const uint32_t part = tid & 3;                  // which quarter of the dimensions
-  const bool qok = qi < L;
+  const bool qok = present(qi);
 
   float q[DL], acc[DL];
   {
@@ -63,13 +72,17 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const uint32_t nkb = (L + KB - 1) / KB;
   for (uint32_t kb = 0; kb < nkb; ++kb) {
     __syncthreads();   // previous block fully consumed
+    if (tid < 64) {
+      const uint64_t bits = __ballot(tid < KB && present(kb * KB + tid));
+      if (tid == 0) kmask = (uint32_t)bits;
+    }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const uint32_t ch = tid + i * 256;
       const uint32_t r = ch / CPR, cc = ch % CPR;
       const uint32_t key = kb * KB + r;
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (key < L) {
+      if (present(key)) {
         kv = *(const float4*)(kg + a.mqk.row_off(key) + cc * 4);
         vv = *(const float4*)(vg + a.mv.row_off(key) + cc * 4);
       }
@@ -77,6 +90,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       *(float4*)(vs + r * D + cc * 4) = vv;
     }
     __syncthreads();
+    const uint32_t km = kmask;
 
     float sc[KB];
     float mx = -INFINITY;
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       for (int i = 0; i < DL; ++i) d0 = fmaf(q[i], kr[i], d0);
       d0 += __shfl_xor(d0, 1, 64);
       d0 += __shfl_xor(d0, 2, 64);
-      sc[j] = (kb * KB + j < L) ? d0 * c : -INFINITY;
+      sc[j] = ((km >> j) & 1) ? d0 * c : -INFINITY;
       mx = fmaxf(mx, sc[j]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -124,7 +138,10 @@ template <int D>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+  if (a.cut.on)
+    hipLaunchKernelGGL((attn_f32_kernel<D, true>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<D, false>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -3,6 +3,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "squad.h"
 #include "squad_kernels.h"
 
@@ -12,22 +15,27 @@ namespace {
 
 struct Geo {
   int64_t T, H, W, tt, th, tw;  // grid and tile
-  int64_t nt, nh, nw;           // window grid
-  int64_t G, Wn, n;             // windows, tokens per window, tokens
+  int64_t nt, nh, nw;           // window grid (cut tilings: rounded up)
+  int64_t G, Wn, n;             // windows, tile cells per window, tokens
+  bool cut;                     // the grid is not a whole number of tiles
 };
 
-int make_geo(const int32_t grid[3], const int32_t tile[3], Geo& g) {
+// cut: whether the entry point accepts grids that are not a whole number of tiles
+// (read as padded up to one with absent tokens; only the forward family does)
+int make_geo(const int32_t grid[3], const int32_t tile[3], Geo& g, bool cut = false) {
   if (!grid || !tile) return SQUAD_ERR_INVALID_ARG;
   for (int i = 0; i < 3; ++i)
     if (grid[i] <= 0 || tile[i] <= 0) return SQUAD_ERR_INVALID_ARG;
   g.T = grid[0]; g.H = grid[1]; g.W = grid[2];
   g.tt = tile[0]; g.th = tile[1]; g.tw = tile[2];
-  if (g.T % g.tt || g.H % g.th || g.W % g.tw) return SQUAD_ERR_SHAPE;
-  g.nt = g.T / g.tt; g.nh = g.H / g.th; g.nw = g.W / g.tw;
+  g.cut = g.T % g.tt || g.H % g.th || g.W % g.tw;
+  if (g.cut && !cut) return SQUAD_ERR_SHAPE;
+  if (g.tt > g.T || g.th > g.H || g.tw > g.W) return SQUAD_ERR_SHAPE;
+  g.nt = (g.T + g.tt - 1) / g.tt; g.nh = (g.H + g.th - 1) / g.th; g.nw = (g.W + g.tw - 1) / g.tw;
   g.n = g.T * g.H * g.W;
   g.Wn = g.tt * g.th * g.tw;
   g.G = g.nt * g.nh * g.nw;
-  if (g.n >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  if (g.G * g.Wn >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   return SQUAD_OK;
 }
 
@@ -134,17 +142,24 @@ bool too_many_units(uint64_t bh, uint64_t units_per_bh, uint64_t rows) {
 }
 
 // Shared checks of the grid/tile entry points: geometry, dtype, sizes, pointers.
+// bytes: one token-order tensor; wbytes: the forward's workspace (the local output
+// in group-major order, one row per tile cell, absent cells included).
 int check_grid_call(const int32_t grid[3], const int32_t tile[3], int32_t heads, int32_t batch,
-                    int32_t head_dim, int32_t dtype, Geo& g, size_t& bytes) {
-  int st = make_geo(grid, tile, g);
+                    int32_t head_dim, int32_t dtype, Geo& g, size_t& bytes, size_t* wbytes = nullptr,
+                    bool cut = false) {
+  int st = make_geo(grid, tile, g, cut);
   if (st) return st;
   st = check_common(heads, batch, head_dim, dtype);
   if (st) return st;
   const uint64_t bh = (uint64_t)heads * (uint64_t)batch;
-  if (too_many_units(bh, (uint64_t)(g.G > g.Wn ? g.G : g.Wn), bh * (uint64_t)g.n)) return SQUAD_ERR_SHAPE;
+  const uint64_t cells = (uint64_t)g.G * (uint64_t)g.Wn;
+  if (too_many_units(bh, (uint64_t)(g.G > g.Wn ? g.G : g.Wn), bh * cells)) return SQUAD_ERR_SHAPE;
   // the kernels address rows inside one batch element with 32-bit offsets
-  if ((uint64_t)g.n * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  if (cells * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  // cut tilings mark absent rows in the per-unit row tables of the 16-bit engine
+  if (g.cut && dtype == SQUAD_DTYPE_BF16 && (g.G > 512 || g.Wn > 512)) return SQUAD_ERR_UNSUPPORTED;
   bytes = (size_t)bh * (size_t)g.n * (size_t)head_dim * elem_bytes(dtype);
+  if (wbytes) *wbytes = (size_t)bh * (size_t)cells * (size_t)head_dim * elem_bytes(dtype);
   return SQUAD_OK;
 }
 
@@ -197,9 +212,9 @@ const char* squad_status_string(int status) {
 size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
                                  int32_t batch, int32_t head_dim, int32_t dtype) {
   Geo g;
-  size_t bytes = 0;
-  if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes)) return 0;
-  return bytes;
+  size_t bytes = 0, wbytes = 0;
+  if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, &wbytes, true)) return 0;
+  return wbytes;
 }
 
 }  // extern "C"
@@ -211,8 +226,8 @@ namespace {
 int check_forward(const void* const* in, int nin, const void* out, const int32_t grid[3],
                   const int32_t tile[3], int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype,
                   float scale, const void* workspace, size_t workspace_bytes, Geo& g) {
-  size_t bytes = 0;
-  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  size_t bytes = 0, wbytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, &wbytes, true);
   if (st) return st;
   for (int i = 0; i < nin; ++i)
     if (!in[i]) return SQUAD_ERR_INVALID_ARG;
@@ -223,13 +238,27 @@ int check_forward(const void* const* in, int nin, const void* out, const int32_t
     for (int i = 0; i < nin; ++i)
       if (misaligned(in[i])) return SQUAD_ERR_ALIGN;
   }
-  if (!workspace || workspace_bytes < bytes) return SQUAD_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < wbytes) return SQUAD_ERR_WORKSPACE;
   if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
   for (int i = 0; i < nin; ++i)
-    if (overlap(in[i], bytes, workspace, bytes)) return SQUAD_ERR_ALIAS;
-  if (out && overlap(out, bytes, workspace, bytes)) return SQUAD_ERR_ALIAS;
+    if (overlap(in[i], bytes, workspace, wbytes)) return SQUAD_ERR_ALIAS;
+  if (out && overlap(out, bytes, workspace, wbytes)) return SQUAD_ERR_ALIAS;
   if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
   return SQUAD_OK;
+}
+
+// Cut tilings: a row is present iff its token lies inside the grid.  Token
+// coordinate on each axis = window digit * tile size + offset digit; the local
+// pass's units are windows (rows offsets), the global pass's the reverse.
+void set_cut(AttnArgs& a, const Geo& g, bool by_window) {
+  if (!g.cut) return;
+  a.cut.on = 1;
+  a.cut.lim[0] = (uint32_t)g.T; a.cut.lim[1] = (uint32_t)g.H; a.cut.lim[2] = (uint32_t)g.W;
+  const uint32_t tl[3] = {(uint32_t)g.tt, (uint32_t)g.th, (uint32_t)g.tw};
+  for (int i = 0; i < 3; ++i) {
+    a.cut.su[i] = by_window ? tl[i] : 1;
+    a.cut.sr[i] = by_window ? 1 : tl[i];
+  }
 }
 
 // Local pass of the forward: units = windows, rows = offsets; the output goes to the
@@ -241,6 +270,7 @@ int forward_local(const void* q, const void* k, const void* v, const Geo& g, int
   a.mqk = token_map(g, heads, head_dim, true);
   a.mv = a.mqk;
   a.mo = group_major_map(g, heads, head_dim, true);
+  set_cut(a, g, true);
   return run_attn(a, head_dim, dtype, s, VType::kBf16ToF16);
 }
 
@@ -252,6 +282,7 @@ int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_
   a.mqk = token_map(g, heads, head_dim, false);
   a.mv = group_major_map(g, heads, head_dim, false);
   a.mo = a.mqk;
+  set_cut(a, g, false);
   return run_attn(a, head_dim, dtype, s, VType::kF16ToBf16);
 }
 
@@ -305,7 +336,7 @@ int squad_local_pass(const void* q, const void* k, const void* v, const int32_t 
                      int32_t head_dim, int32_t dtype, float scale, squad_stream_t stream) {
   Geo g;
   size_t bytes = 0;
-  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true);
   if (st) return st;
   const void* in[3] = {q, k, v};
   st = check_ptrs(in, 3, o1, bytes);
@@ -315,6 +346,7 @@ int squad_local_pass(const void* q, const void* k, const void* v, const int32_t 
   a.mqk = token_map(g, heads, head_dim, true);
   a.mv = a.mqk;
   a.mo = a.mqk;
+  set_cut(a, g, true);
   return run_attn(a, head_dim, dtype, (hipStream_t)stream);
 }
 
@@ -323,7 +355,7 @@ int squad_global_pass(const void* q, const void* k, const void* vstream, const i
                       int32_t head_dim, int32_t dtype, float scale, squad_stream_t stream) {
   Geo g;
   size_t bytes = 0;
-  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes);
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true);
   if (st) return st;
   const void* in[3] = {q, k, vstream};
   st = check_ptrs(in, 3, out, bytes);
@@ -333,6 +365,7 @@ int squad_global_pass(const void* q, const void* k, const void* vstream, const i
   a.mqk = token_map(g, heads, head_dim, false);
   a.mv = a.mqk;
   a.mo = a.mqk;
+  set_cut(a, g, false);
   return run_attn(a, head_dim, dtype, (hipStream_t)stream);
 }
 
@@ -423,11 +456,50 @@ int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* 
   return run_attn(a, head_dim, dtype, (hipStream_t)stream);
 }
 
+int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]) {
+  if (!grid || !tile_out) return SQUAD_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (grid[i] <= 0) return SQUAD_ERR_INVALID_ARG;
+  const uint64_t n = (uint64_t)grid[0] * (uint64_t)grid[1] * (uint64_t)grid[2];
+  if (n >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  // per axis, the smallest tile for each number of windows k: ceil(X / k)
+  std::vector<int64_t> cand[3];
+  for (int i = 0; i < 3; ++i) {
+    const int64_t X = grid[i];
+    for (int64_t k = 1; k <= X; ++k) {
+      const int64_t t = (X + k - 1) / k;
+      if (cand[i].empty() || cand[i].back() != t) cand[i].push_back(t);
+      // beyond sqrt(X) consecutive k give the same t; jump to the next change
+      if (t > 1) k = std::max(k, (X + t - 2) / (t - 1) - 1);
+    }
+    std::sort(cand[i].begin(), cand[i].end());
+    cand[i].erase(std::unique(cand[i].begin(), cand[i].end()), cand[i].end());
+  }
+  uint64_t best_cost = ~uint64_t(0), best_pad = ~uint64_t(0);
+  int64_t best[3] = {grid[0], grid[1], grid[2]};
+  for (int64_t tt : cand[0])
+    for (int64_t th : cand[1])
+      for (int64_t tw : cand[2]) {
+        const uint64_t wn = (uint64_t)(tt * th * tw);
+        const uint64_t gp = (uint64_t)(((grid[0] + tt - 1) / tt) * ((grid[1] + th - 1) / th) *
+                                       ((grid[2] + tw - 1) / tw));
+        const uint64_t cost = gp * wn * (wn + gp);
+        const uint64_t pad = gp * wn - n;
+        if (cost < best_cost || (cost == best_cost && pad < best_pad)) {
+          best_cost = cost;
+          best_pad = pad;
+          best[0] = tt; best[1] = th; best[2] = tw;
+        }
+      }
+  for (int i = 0; i < 3; ++i) tile_out[i] = (int32_t)best[i];
+  return SQUAD_OK;
+}
+
 int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t tile[3], int32_t heads,
                             int32_t batch, int32_t head_dim, int64_t* offsets) {
   Geo g;
   size_t bytes = 0;
-  int st = check_grid_call(grid, tile, heads, batch, head_dim, SQUAD_DTYPE_BF16, g, bytes);
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, SQUAD_DTYPE_F32, g, bytes, nullptr, true);
   if (st) return st;
   if (!offsets) return SQUAD_ERR_INVALID_ARG;
   RowMap m;
@@ -439,12 +511,18 @@ int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t 
     case 3: m = group_major_map(g, heads, head_dim, false); U = (uint32_t)g.Wn; L = (uint32_t)g.G; break;
     default: return SQUAD_ERR_INVALID_ARG;
   }
+  // the token maps of a cut tiling: absent rows read -1, through the kernels' own test
+  AttnArgs a{};
+  a.mqk = m;
+  if (which < 2) set_cut(a, g, which == 0);
   size_t i = 0;
   for (uint32_t b = 0; b < (uint32_t)batch; ++b)
     for (uint32_t h = 0; h < (uint32_t)heads; ++h)
       for (uint32_t s = 0; s < U; ++s) {
         const int64_t base = m.base(b, h, s);
-        for (uint32_t r = 0; r < L; ++r) offsets[i++] = base + m.row_off(r);
+        const UnitDigits ud = cut_unit_digits(a, s);
+        for (uint32_t r = 0; r < L; ++r)
+          offsets[i++] = (!a.cut.on || cut_present(a, ud, r)) ? base + m.row_off(r) : -1;
       }
   return SQUAD_OK;
 }

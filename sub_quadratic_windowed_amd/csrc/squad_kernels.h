@@ -14,6 +14,17 @@ namespace squad {
 // bh = batch * heads + head), so neighbouring units are the heads of one window or
 // group.  Rows of q and k are located with mqk, rows of v with mv, output rows
 // with mo.
+// Tilings cut by the grid edge: a grid that is not a whole number of tiles is
+// padded up to one with absent tokens.  Row r of unit s is present iff, on every
+// axis (t, h, w), unit digit * su + row digit * sr < lim, where the digits are
+// those of the token map (unit: window or offset digits, row: the other kind).
+struct Cut {
+  uint32_t on;       // nonzero: some rows are absent
+  uint32_t lim[3];   // T, H, W
+  uint32_t su[3];    // per-axis scale of the unit's digit
+  uint32_t sr[3];    // per-axis scale of the row's digit
+};
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -29,7 +40,26 @@ struct AttnArgs {
   uint32_t nchunks;  // query chunks per unit (set by the launcher)
   uint32_t v_like_k; // nonzero: mv locates rows exactly as mqk does
   float c;           // softmax scale * log2(e)
+  Cut cut;           // absent rows (cut tilings only; on == 0 otherwise)
 };
+
+// The digits of unit s under the token map, for Cut tests of its rows.
+struct UnitDigits {
+  uint32_t d[3];
+};
+__host__ __device__ __forceinline__ UnitDigits cut_unit_digits(const AttnArgs& a, uint32_t s) {
+  UnitDigits u;
+  a.mqk.unit.digits(s, u.d[0], u.d[1], u.d[2]);
+  return u;
+}
+// Whether row r (< L) of the unit is a token of the grid.
+__host__ __device__ __forceinline__ bool cut_present(const AttnArgs& a, const UnitDigits& u, uint32_t r) {
+  uint32_t r2, r1, r0;
+  a.mqk.row.digits(r, r2, r1, r0);
+  return u.d[0] * a.cut.su[0] + r2 * a.cut.sr[0] < a.cut.lim[0] &&
+         u.d[1] * a.cut.su[1] + r1 * a.cut.sr[1] < a.cut.lim[1] &&
+         u.d[2] * a.cut.su[2] + r0 * a.cut.sr[2] < a.cut.lim[2];
+}
 
 // Value and output types of the bf16 engine (q and k are always bf16).  The local
 // pass of squad_attn_forward writes its output as fp16 (three more significand bits

@@ -90,6 +90,13 @@ struct Mix {
     uint32_t d1 = q0 - q1 * x1.d;
     return (int64_t)q1 * s2 + (int64_t)d1 * s1 + (int64_t)d0 * s0;
   }
+  // the digits (x2, x1, x0) of x
+  __host__ __device__ __forceinline__ void digits(uint32_t x, uint32_t& x2, uint32_t& x1d, uint32_t& x0d) const {
+    const uint32_t q0 = x0.div(x);
+    x0d = x - q0 * x0.d;
+    x2 = x1.div(q0);
+    x1d = q0 - x2 * x1.d;
+  }
 };
 
 // Row part of a map: evaluated per key block in the attention loop, 32-bit (the
@@ -104,6 +111,12 @@ struct Mix32 {
     uint32_t q1 = x1.div(q0);
     uint32_t d1 = q0 - q1 * x1.d;
     return (int32_t)(q1 * (uint32_t)s2 + d1 * (uint32_t)s1 + d0 * (uint32_t)s0);
+  }
+  __host__ __device__ __forceinline__ void digits(uint32_t x, uint32_t& x2, uint32_t& x1d, uint32_t& x0d) const {
+    const uint32_t q0 = x0.div(x);
+    x0d = x - q0 * x0.d;
+    x2 = x1.div(q0);
+    x1d = q0 - x2 * x1.d;
   }
 };
 

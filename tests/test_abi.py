@@ -42,7 +42,11 @@ def test_status_strings():
 def test_workspace_size():
     assert sq.squad_attn_workspace_size((64, 48, 80), (4, 12, 10), 24, 1, 128, 1) == 245760 * 24 * 128 * 2
     assert sq.squad_attn_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 64, 0) == 256 * 2 * 64 * 4
-    assert sq.squad_attn_workspace_size((4, 8, 8), (3, 4, 4), 2, 1, 64, 0) == 0
+    # a cut tiling: 2 x 2 x 2 windows of 48 cells, absent cells included
+    assert sq.squad_attn_workspace_size((4, 8, 8), (3, 4, 4), 2, 1, 64, 0) == 8 * 48 * 2 * 64 * 4
+    assert sq.squad_attn_workspace_size((4, 8, 8), (5, 4, 4), 2, 1, 64, 0) == 0    # tile larger than the grid
+    assert sq.squad_attn_workspace_size((33, 32, 32), (2, 1, 1), 1, 1, 64, 1) == 0  # bf16 cut: G > 512
+    assert sq.squad_attn_workspace_size((33, 32, 32), (2, 1, 1), 1, 1, 64, 0) == 17 * 32 * 32 * 2 * 64 * 4
     assert sq.squad_attn_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 96, 1) == 0
 
 
@@ -64,7 +68,9 @@ def fwd(q=A, k=B, v=C, grid=(4, 8, 8), tile=(1, 4, 4), heads=2, out=O, batch=1, 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), INVALID), (dict(out=0), INVALID), (dict(heads=0), INVALID), (dict(batch=-1), INVALID),
     (dict(grid=(4, 0, 8)), INVALID), (dict(tile=(1, 4, -4)), INVALID),
-    (dict(tile=(3, 4, 4)), SHAPE), (dict(tile=(1, 5, 4)), SHAPE), (dict(grid=(1 << 11, 1 << 11, 1 << 10)), SHAPE),
+    (dict(tile=(5, 4, 4)), SHAPE), (dict(tile=(1, 9, 4)), SHAPE), (dict(grid=(1 << 11, 1 << 11, 1 << 10)), SHAPE),
+    (dict(grid=(33, 32, 32), tile=(2, 1, 1)), UNSUP),
+    (dict(tile=(3, 4, 4), ws_bytes=8 * 48 * 2 * 64 * 2 - 1), WORKSPACE),
     (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(dtype=2), UNSUP),
     (dict(q=A + 8), ALIGN), (dict(out=O + 4), ALIGN), (dict(ws=WS + 2), ALIGN),
     (dict(out=A), ALIAS), (dict(out=B + 64), ALIAS), (dict(ws=C), ALIAS), (dict(ws=O), ALIAS),
@@ -155,3 +161,82 @@ def _device_count():
 @pytest.mark.skipif(_device_count() > 0, reason="fake pointers must never reach a real device")
 def test_valid_call_without_device_reports_hip_error():
     assert fwd() == HIP
+
+
+# ---------------------------------------------------------------- tile planner (host-only)
+
+def _plan_cost(grid, tile):
+    wn = int(np.prod(tile))
+    gp = int(np.prod([-(-g // t) for g, t in zip(grid, tile)]))
+    return gp * wn * (wn + gp), gp * wn - int(np.prod(grid))
+
+
+@pytest.mark.parametrize("grid", [(64, 48, 80), (32, 24, 40), (16, 16, 16), (4, 8, 8), (21, 45, 80),
+                                  (7, 7, 7), (1, 1, 1), (5, 3, 1), (2, 1, 97)])
+def test_plan_tile_is_the_cheapest_tiling(grid):
+    """Brute force over every tile no larger than the grid: the planner's pick has
+    the least product work, and the fewest absent cells among the cheapest."""
+    tile = sq.squad_plan_tile(grid)
+    assert all(1 <= t <= g for t, g in zip(tile, grid))
+    best = min(_plan_cost(grid, (a, b, c)) for a in range(1, grid[0] + 1)
+               for b in range(1, grid[1] + 1) for c in range(1, grid[2] + 1))
+    assert _plan_cost(grid, tile) == best
+
+
+def test_plan_tile_near_sqrt_n():
+    # whole tilings with W = G = sqrt(n) exist for these grids; the planner finds one
+    for grid in [(16, 16, 16), (4, 8, 8), (1, 64, 64)]:
+        tile = sq.squad_plan_tile(grid)
+        n = int(np.prod(grid))
+        assert int(np.prod(tile)) ** 2 == n and _plan_cost(grid, tile)[1] == 0
+
+
+def test_plan_tile_rejects_bad_grids():
+    lib = _lib.lib()
+    out = (ctypes.c_int32 * 3)()
+    assert lib.squad_plan_tile(_lib.int3((4, 0, 8)), out) == INVALID
+    assert lib.squad_plan_tile(_lib.int3((1 << 11, 1 << 11, 1 << 10)), out) == SHAPE
+
+
+# ---------------------------------------------------------------- cut tilings: the kernels' presence test
+
+CUT_MAP_SHAPES = [((3, 5, 7), (2, 2, 3)), ((5, 12, 20), (2, 5, 6)), ((4, 8, 8), (3, 4, 4)),
+                  ((2, 3, 4), (2, 3, 3)), ((7, 7, 7), (1, 2, 7)), ((33, 32, 32), (2, 1, 1))]
+
+
+@pytest.mark.parametrize("grid,tile", CUT_MAP_SHAPES)
+def test_cut_row_maps_are_the_padded_partition(grid, tile):
+    """On a cut tiling the token maps, with the presence test the kernels use to skip
+    absent rows, are the oracle's padded window partition: -1 exactly at absent
+    cells, the token's row elsewhere; the workspace maps stay a bijection over all
+    tile cells."""
+    heads, batch, d = 2, 2, 64
+    idx = oracle.padded_window_index(grid, tile)          # [G, Wn], -1 for absent cells
+    G, Wn = idx.shape
+    n = int(np.prod(grid))
+    b = np.arange(batch)[:, None, None, None]
+    h = np.arange(heads)[None, :, None, None]
+    want0 = np.where(idx[None, None] >= 0, ((b * n + idx[None, None]) * heads + h) * d, -1)
+    got0 = sq.squad_debug_row_offsets(0, grid, tile, heads, batch, d).reshape(batch, heads, G, Wn)
+    assert np.array_equal(got0, want0)
+    got1 = sq.squad_debug_row_offsets(1, grid, tile, heads, batch, d).reshape(batch, heads, Wn, G)
+    assert np.array_equal(got1, np.swapaxes(want0, 2, 3))
+    # row 0 of every unit is present (the kernels' clamp target for absent queries)
+    assert (got0[:, :, :, 0] >= 0).all() and (got1[:, :, :, 0] >= 0).all()
+    for which in (2, 3):
+        got = sq.squad_debug_row_offsets(which, grid, tile, heads, batch, d)
+        assert np.array_equal(np.sort(got), np.arange(batch * heads * G * Wn) * d)
+
+
+def test_cut_tilings_at_the_half_pass_entry_points():
+    lib = _lib.lib()
+    p = ctypes.c_void_p
+    t = _lib.int3((2, 3, 3))
+    for fn in (lib.squad_local_pass, lib.squad_global_pass):
+        # accepted up to the device call (fake pointers: HIP error without a device)
+        if _device_count() == 0:
+            assert fn(p(A), p(B), p(C), _lib.int3((3, 5, 7)), t, 2, p(O), 1, 64, 1, ctypes.c_float(0), None) == HIP
+        assert fn(p(A), p(B), p(C), _lib.int3((33, 32, 32)), _lib.int3((2, 1, 1)), 1, p(O), 1, 64, 1,
+                  ctypes.c_float(0), None) == UNSUP
+    for fn in (lib.squad_tile_gather, lib.squad_tile_scatter, lib.squad_window_to_group):
+        assert fn(p(A), p(B), _lib.int3((3, 5, 7)), t, 2, 1, 64, 1, None) == SHAPE

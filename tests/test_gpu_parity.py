@@ -316,3 +316,85 @@ def test_forward_halves_compose_to_the_forward():
     o1 = ws.view(torch.float16).reshape(2, 3, 60, 16, 128)
     want = oracle.tile_gather(oracle.local_pass(f64(q), f64(k), f64(v), grid, tile), grid, tile)
     assert maxerr(o1.transpose(2, 3), want) <= TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- cut tilings (grid not a whole number of tiles)
+
+CUT_CASES = [
+    # grid, tile, batch, heads, head_dim, dtype, peaky
+    ((3, 5, 7), (2, 2, 3), 1, 2, 64, torch.float32, False),       # cut on every axis, Wn = 12, G = 18
+    ((3, 5, 7), (2, 2, 3), 2, 2, 128, torch.bfloat16, True),
+    ((5, 12, 20), (2, 5, 6), 1, 2, 128, torch.bfloat16, False),   # Wn = 60, G = 36
+    ((5, 12, 20), (2, 5, 6), 1, 1, 64, torch.float32, True),
+    ((4, 8, 8), (3, 4, 4), 1, 2, 64, torch.bfloat16, False),      # cut along t only
+    ((7, 7, 7), (1, 2, 7), 1, 2, 128, torch.bfloat16, False),     # the planner's tile for 7^3
+    ((9, 19, 21), (5, 10, 10), 1, 2, 128, torch.bfloat16, False), # Wn = 500 (16 key blocks), G = 12
+    ((3, 17, 30), (2, 16, 16), 1, 1, 64, torch.bfloat16, True),   # Wn = 512, G = 8
+    ((8, 15, 15), (1, 2, 2), 1, 2, 128, torch.bfloat16, False),   # G = 512 groups of 1..4 present rows
+    ((9, 32, 32), (2, 1, 1), 1, 1, 64, torch.float32, False),     # fp32: G = 5120 rows per group
+    ((21, 45, 80), (3, 9, 10), 1, 2, 128, torch.bfloat16, False), # the planner's tile: Wn = 270, G = 280
+]
+
+
+@pytest.mark.parametrize("case", CUT_CASES, ids=lambda c: f"{c[0]}-{c[1]}-b{c[2]}h{c[3]}d{c[4]}-{str(c[5])[6:]}")
+def test_cut_forward_matches_oracle(case):
+    grid, tile, B, Hh, d, dtype, peaky = case
+    n = grid[0] * grid[1] * grid[2]
+    q, k, v = rand_inputs((B, n, Hh, d), dtype, 21, peaky)
+    say(f"cut forward {case}")
+    out = sq.squad_attn_forward(q, k, v, grid, tile, Hh)
+    torch.cuda.synchronize()
+    want = oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)
+    err = maxerr(out, want)
+    say(f"  max-abs {err:.3e}")
+    assert np.isfinite(f64(out)).all()
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("case", CUT_CASES[:6], ids=lambda c: f"{c[0]}-{c[1]}-{str(c[5])[6:]}")
+def test_cut_each_pass_matches_oracle(case):
+    """The half-pass entry points on cut tilings, every present token written."""
+    grid, tile, B, Hh, d, dtype, peaky = case
+    n = grid[0] * grid[1] * grid[2]
+    q, k, v = rand_inputs((B, n, Hh, d), dtype, 22, peaky)
+    say(f"cut passes {case}")
+    nanfill = torch.full((B, n, Hh, d), float("nan"), dtype=dtype, device="cuda")
+    o1 = sq.squad_local_pass(q, k, v, grid, tile, Hh, out=nanfill.clone())
+    out = sq.squad_global_pass(q, k, v, grid, tile, Hh, out=nanfill.clone())
+    torch.cuda.synchronize()
+    qq, kk, vv = f64(q), f64(k), f64(v)
+    assert maxerr(o1, oracle.local_pass(qq, kk, vv, grid, tile)) <= TOL[dtype]
+    assert maxerr(out, oracle.global_pass(qq, kk, vv, grid, tile)) <= TOL[dtype]
+
+
+def test_cut_forward_halves_compose_and_fill_the_workspace():
+    """On a cut tiling the two halves give the forward bit for bit, and the workspace
+    holds the local output at every present cell (absent cells are not read)."""
+    grid, tile = (5, 12, 20), (2, 5, 6)
+    B, Hh, d = 2, 3, 128
+    q, k, v = rand_inputs((B, 1200, Hh, d), torch.bfloat16, 23, True)
+    out = sq.squad_attn_forward(q, k, v, grid, tile)
+    ws = sq.squad_attn_forward_local(q, k, v, grid, tile)
+    out2 = sq.squad_attn_forward_global(q, k, grid, tile, ws)
+    assert torch.equal(out, out2)
+    idx = oracle.padded_window_index(grid, tile)     # [G, Wn], -1 for absent cells
+    G, Wn = idx.shape
+    o1 = ws.view(torch.float16).reshape(B, Hh, Wn, G, d).transpose(2, 3)   # [B, Hh, G, Wn, d]
+    want = oracle.local_pass(f64(q), f64(k), f64(v), grid, tile)           # token order
+    present = idx >= 0
+    got = f64(o1)[:, :, present]                                           # [B, Hh, n, d] in window order
+    exp = np.transpose(want, (0, 2, 1, 3))[:, :, idx[present]]
+    assert np.max(np.abs(got - exp)) <= TOL[torch.bfloat16]
+
+
+def test_cut_forward_on_the_planners_tile():
+    """squad_plan_tile's pick for a grid with no whole tiling near sqrt(n) runs and
+    matches the oracle."""
+    grid = (11, 13, 17)
+    tile = sq.squad_plan_tile(grid)
+    n = grid[0] * grid[1] * grid[2]
+    q, k, v = rand_inputs((1, n, 2, 128), torch.bfloat16, 24)
+    say(f"planner tile {grid} -> {tile}")
+    out = sq.squad_attn_forward(q, k, v, grid, tile)
+    torch.cuda.synchronize()
+    assert maxerr(out, oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)) <= TOL[torch.bfloat16]
