@@ -12,6 +12,8 @@ Beside it: achieved TFLOP/s and the fraction of the bf16 dense MFMA peak, the
 roofline object of the dominant kernel (its average duration from HIP events on
 the launch stream), the float64 CPU oracle timed on a bounded sample of the same
 workload, and a dense full-attention comparator on the 5B-DiT-shaped workload.
+Under `tilings`, the same inputs under the planner's compact tile and on a grid
+cut by the tiling (one column narrower).
 """
 
 import argparse
@@ -38,6 +40,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-permutations", action="store_true")
+    p.add_argument("--no-tilings", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's timed sample")
     return p.parse_args()
 
@@ -197,6 +200,11 @@ def main():
     if not args.no_permutations:
         perms = permutation_rates(sq, cfg, q, stream)
 
+    tilings = None
+    if not args.no_tilings and cfg.name == "highres_bf16":
+        print("[bench] other tilings of the workload", file=sys.stderr, flush=True)
+        tilings = tiling_rates(sq, q, k, v, H, stream)
+
     dense = None
     if not args.no_dense:
         del out, ws
@@ -235,6 +243,7 @@ def main():
         "cpu_baseline": base,
         "dense_comparator": dense,
         "permutations": perms,
+        "tilings": tilings,
     }
     print(json.dumps(line), flush=True)
 
@@ -262,6 +271,48 @@ def permutation_rates(sq, cfg, q, stream):
         out[name] = {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
                      "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del win, grp, tok
+    return out
+
+
+def present_pairs(grid, tile):
+    """(sum over windows of present^2, sum over offset groups of present^2): the
+    query-key pairs of the two passes on a possibly cut tiling.  Separable by axis:
+    a window's present count is the product of its per-axis extents, an offset
+    group's the product of per-axis counts of windows that reach that offset."""
+    win = grp = 1
+    for X, t in zip(grid, tile):
+        k = -(-X // t)
+        ext = [t] * (k - 1) + [X - t * (k - 1)]
+        win *= sum(e * e for e in ext)
+        grp *= sum(sum(1 for e in ext if e > a) ** 2 for a in range(t))
+    return win, grp
+
+
+def tiling_rates(sq, q, k, v, heads, stream):
+    """Forward time on the workload's inputs under two more tilings of the same
+    window size: the compact tile the planner picks for the grid (whole), and the
+    grid one column narrower (64 x 48 x 79: the last column of windows is cut to 9
+    of 10 cells, so every global group of offsets w = 9 loses one row)."""
+    import torch
+
+    d = q.shape[-1]
+    out = {}
+    for name, grid, tile in (("whole_planner", (64, 48, 80), tuple(sq.squad_plan_tile((64, 48, 80)))),
+                             ("cut_w", (64, 48, 79), (8, 6, 10))):
+        n = grid[0] * grid[1] * grid[2]
+        qs, ks, vs = q[:, :n], k[:, :n], v[:, :n]     # the first n tokens (batch 1: contiguous)
+        o = torch.empty_like(qs)
+        ws = torch.empty(sq.squad_attn_workspace_size(grid, tile, heads, 1, d, qs.dtype), dtype=torch.uint8,
+                         device=q.device)
+        fwd = lambda: sq.squad_attn_forward(qs, ks, vs, grid, tile, heads, out=o, workspace=ws, stream=stream)
+        fwd()
+        torch.cuda.synchronize()
+        ms = time_launches(fwd, stream, 20)
+        pw, pg = present_pairs(grid, tile)
+        flops = 4.0 * d * heads * (pw + pg)
+        out[name] = {"grid": list(grid), "tile": list(tile), "ms": round(ms, 4),
+                     "tokens_per_s": round(n / (ms * 1e-3), 1), "tflops": round(flops / ms / 1e9, 1)}
+        del o, ws
     return out
 
 

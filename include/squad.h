@@ -135,7 +135,9 @@ size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], i
  * that minimises the forward's product work, proportional to
  * Gp * Wn * (Wn + Gp) with Wn = tt*th*tw and Gp the number of windows of the
  * (possibly cut) tiling; ties go to the tiling with fewer absent tokens, then to
- * the smaller tile in (tt, th, tw) order.  Host-only; writes tile_out[3].
+ * the most compact window (per axis, the tile extent closest to the number of
+ * windows along that axis: least sum of squared log ratios), then to the first
+ * in ascending (tt, th, tw) order.  Host-only; writes tile_out[3].
  * Returns SQUAD_ERR_INVALID_ARG for null pointers or sizes <= 0, SQUAD_ERR_SHAPE
  * for grids of 2^31 tokens or more.
  */

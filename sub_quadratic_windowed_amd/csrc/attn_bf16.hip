@@ -229,8 +229,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // units of at most TABLE_ROWS rows: every row's offset is formed once, into LDS
   __shared__ int32_t ktab[TAB ? TABLE_ROWS : 1];
   __shared__ int32_t vtab[TAB ? TABLE_ROWS : 1];
-  // cut tilings: bit r % 32 of word r / 32 says whether row r is present
-  __shared__ uint32_t rmask[CUT ? TABLE_ROWS / 32 : 1];
+  // cut tilings: which rows are present, per 32-row key block and per lane half.
+  // A lane of half h holds score registers r = 0..15 for the block's rows
+  // 8*(r/4) + 4*h + r%4 (the MFMA output layout); entry 2*kb + h has bit r set
+  // when that row is present, so the score mask tests constant bit positions.
+  __shared__ uint32_t rmask[CUT ? TABLE_ROWS / 16 : 1];
   if constexpr (CUT) {
     // byte offsets; absent rows (and rows past the end, up to a whole block) read row 0
     const uint32_t iters = (nkb * BN + C::NT - 1) / C::NT;
@@ -244,10 +247,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
       }
       const uint64_t bits = __ballot(ok);
+      // this wave's 64 rows are key blocks w0 and w0 + 1; lanes 0..3 each compact
+      // one (block, half) pair: the nibbles at 4*h, 8 + 4*h, 16 + 4*h, 24 + 4*h
       const uint32_t w0 = (i * C::NT + 64 * wave) / 32;
-      if (lane == 0 && w0 < TABLE_ROWS / 32) {
-        rmask[w0] = (uint32_t)bits;
-        if (w0 + 1 < TABLE_ROWS / 32) rmask[w0 + 1] = (uint32_t)(bits >> 32);
+      if (lane < 4 && w0 + (lane >> 1) < TABLE_ROWS / 32) {
+        uint32_t x = (uint32_t)(bits >> (32 * (lane >> 1)));
+        x = (x >> (4 * (lane & 1))) & 0x0f0f0f0fu;
+        x = (x | (x >> 4)) & 0x00ff00ffu;
+        x = (x | (x >> 8)) & 0x0000ffffu;
+        rmask[2 * w0 + lane] = x;
       }
     }
   } else if constexpr (TAB) {
@@ -404,11 +412,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       if (ST == 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
       // keys past the end of the unit take no weight
       if constexpr (CUT) {
-        const uint32_t km = rmask[kb];
-        if (km != 0xffffffffu) {
+        const uint32_t km = rmask[2 * kb + half];
+        if (km != 0xffffu) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (!((km >> (8 * (r / 4) + 4 * half + (r % 4))) & 1)) sc[r] = -INFINITY;
+            if (!__builtin_amdgcn_ubfe(km, r, 1)) sc[r] = -INFINITY;
         }
       } else if ((kb + 1) * BN > L) {
 #pragma unroll
@@ -508,7 +516,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const uint32_t wcol = lane % C::CPR;
     const uint32_t wrow = lane / C::CPR;
     bool qok = q0 + l32 < L;
-    if constexpr (CUT) qok = qok && ((rmask[(q0 + l32) >> 5] >> ((q0 + l32) & 31)) & 1);
+    if constexpr (CUT) {
+      // row x of block x / 32 sits in half (x / 4) % 2 at register 4 * ((x % 32) / 8) + x % 4
+      const uint32_t x = q0 + l32;
+      qok = qok && ((rmask[2 * (x >> 5) + ((x >> 2) & 1)] >> (4 * ((x & 31) >> 3) + (x & 3))) & 1);
+    }
     const int32_t oo = qok ? a.mo.row_off(q0 + l32) : -1;
 #pragma unroll
     for (int i = 0; i < 32 / WR; ++i) {

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "squad.h"
@@ -475,19 +476,34 @@ int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]) {
     std::sort(cand[i].begin(), cand[i].end());
     cand[i].erase(std::unique(cand[i].begin(), cand[i].end()), cand[i].end());
   }
+  // ties: fewer absent tokens, then the most compact window (along every axis the
+  // tile extent closest to the number of windows, in log ratio), then the first in
+  // ascending (tt, th, tw) order
   uint64_t best_cost = ~uint64_t(0), best_pad = ~uint64_t(0);
+  double best_skew = 0.0;
   int64_t best[3] = {grid[0], grid[1], grid[2]};
   for (int64_t tt : cand[0])
     for (int64_t th : cand[1])
       for (int64_t tw : cand[2]) {
-        const uint64_t wn = (uint64_t)(tt * th * tw);
-        const uint64_t gp = (uint64_t)(((grid[0] + tt - 1) / tt) * ((grid[1] + th - 1) / th) *
-                                       ((grid[2] + tw - 1) / tw));
+        const int64_t t[3] = {tt, th, tw};
+        uint64_t wn = 1, gp = 1;
+        double skew = 0.0;
+        for (int i = 0; i < 3; ++i) {
+          const int64_t k = (grid[i] + t[i] - 1) / t[i];
+          wn *= (uint64_t)t[i];
+          gp *= (uint64_t)k;
+          const double l = std::log((double)t[i] / (double)k);
+          skew += l * l;
+        }
         const uint64_t cost = gp * wn * (wn + gp);
         const uint64_t pad = gp * wn - n;
-        if (cost < best_cost || (cost == best_cost && pad < best_pad)) {
+        const bool better = cost != best_cost ? cost < best_cost
+                          : pad != best_pad   ? pad < best_pad
+                                              : skew < best_skew - 1e-12;
+        if (better) {
           best_cost = cost;
           best_pad = pad;
+          best_skew = skew;
           best[0] = tt; best[1] = th; best[2] = tw;
         }
       }

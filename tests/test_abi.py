@@ -178,9 +178,24 @@ def test_plan_tile_is_the_cheapest_tiling(grid):
     the least product work, and the fewest absent cells among the cheapest."""
     tile = sq.squad_plan_tile(grid)
     assert all(1 <= t <= g for t, g in zip(tile, grid))
-    best = min(_plan_cost(grid, (a, b, c)) for a in range(1, grid[0] + 1)
-               for b in range(1, grid[1] + 1) for c in range(1, grid[2] + 1))
+    tiles = [(a, b, c) for a in range(1, grid[0] + 1) for b in range(1, grid[1] + 1) for c in range(1, grid[2] + 1)]
+    best = min(_plan_cost(grid, t) for t in tiles)
     assert _plan_cost(grid, tile) == best
+    # among those, the most compact window: per axis, extent close to the window count
+    skew = min(_skew(grid, t) for t in tiles if _plan_cost(grid, t) == best)
+    assert _skew(grid, tile) <= skew + 1e-9
+
+
+def _skew(grid, tile):
+    return sum(np.log(t / -(-g // t)) ** 2 for g, t in zip(grid, tile))
+
+
+def test_plan_tile_prefers_compact_windows():
+    # equal work and no absent tokens: (8, 6, 10) has 8 x 8 x 8 windows, (4, 12, 10)
+    # and (1, 6, 80) have the same sizes but stretched windows
+    assert sq.squad_plan_tile((64, 48, 80)) == (8, 6, 10)
+    assert sq.squad_plan_tile((16, 16, 16)) == (4, 4, 4)
+    assert sq.squad_plan_tile((64, 32, 32)) == (8, 4, 8)
 
 
 def test_plan_tile_near_sqrt_n():

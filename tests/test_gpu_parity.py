@@ -332,7 +332,7 @@ CUT_CASES = [
     ((3, 17, 30), (2, 16, 16), 1, 1, 64, torch.bfloat16, True),   # Wn = 512, G = 8
     ((8, 15, 15), (1, 2, 2), 1, 2, 128, torch.bfloat16, False),   # G = 512 groups of 1..4 present rows
     ((9, 32, 32), (2, 1, 1), 1, 1, 64, torch.float32, False),     # fp32: G = 5120 rows per group
-    ((21, 45, 80), (3, 9, 10), 1, 2, 128, torch.bfloat16, False), # the planner's tile: Wn = 270, G = 280
+    ((21, 45, 79), (3, 9, 10), 1, 2, 128, torch.bfloat16, False), # n = 74655, Wn = 270, G = 280, cut along w
 ]
 
 
