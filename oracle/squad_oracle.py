@@ -43,6 +43,13 @@ notes of this repository):
   softmax is taken in its max-subtracted form.
 * Batch elements and heads are independent; there is no mask and no causality.
 
+Gradients (squad_backward and the per-pass backwards) are the chain rule applied
+to the definitions above: the pages state no gradient formula, but the distillation
+they run (flow-matching SFT, then DMD2; technical summary, "Methodologie") trains
+through the operator.  q and k receive the sum of both passes' gradients; the
+global pass's value gradient is the upstream gradient of the local output.
+squad_forward_stats gives each row's softmax normaliser (log-sum-exp) per pass.
+
 All arithmetic is float64.  Every function below is written from the definition,
 with numpy fancy indexing and numpy matmul as its only library steps.
 """
@@ -65,6 +72,11 @@ __all__ = [
     "tile_scatter",
     "window_to_group",
     "window_attn",
+    "softmax_attention_backward",
+    "local_pass_backward",
+    "global_pass_backward",
+    "squad_backward",
+    "squad_forward_stats",
 ]
 
 
@@ -290,3 +302,103 @@ def window_attn(q, k, v, scale=None) -> np.ndarray:
     q = np.asarray(q, dtype=np.float64)
     s = _default_scale(q.shape[-1], scale)
     return softmax_attention(q, k, v, s)
+
+
+# ---- gradients (the fine-tuning the pages run, flow-matching SFT and DMD2 in the
+# technical summary's "Methodologie" and "Experimentele Resultaten", needs the
+# operator's gradients; the pages give no formula, so these are the chain rule
+# applied to the definitions above) ----
+
+def softmax_attention_backward(q, k, v, dout, scale):
+    """Gradients of softmax_attention with respect to q, k and v, in float64.
+
+    With l = scale * q k^T, a = softmax over the key axis, o = a v and an upstream
+    gradient dout:
+      dv = a^T dout;  da = dout v^T;
+      dl_ij = a_ij * (da_ij - sum_m a_im da_im)   (the softmax Jacobian; the sum
+              equals <dout_i, o_i>);
+      dq = scale * dl k;  dk = scale * dl^T q.
+    Shapes as in softmax_attention; returns (dq, dk, dv).
+    """
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    logits = float(scale) * np.matmul(q, np.swapaxes(k, -1, -2))
+    logits = logits - logits.max(axis=-1, keepdims=True)
+    a = np.exp(logits)
+    a = a / a.sum(axis=-1, keepdims=True)
+    dv = np.matmul(np.swapaxes(a, -1, -2), dout)
+    da = np.matmul(dout, np.swapaxes(v, -1, -2))
+    dl = a * (da - (a * da).sum(axis=-1, keepdims=True))
+    dq = float(scale) * np.matmul(dl, k)
+    dk = float(scale) * np.matmul(np.swapaxes(dl, -1, -2), q)
+    return dq, dk, dv
+
+
+def _units_backward(q, k, v, dout, units, s):
+    """softmax_attention_backward inside each unit (a row of `units`, -1 = absent)."""
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    if (units >= 0).all():
+        # [B, U, L, Hh, d] -> [B, Hh, U, L, d]
+        g = lambda x: x[:, units].transpose(0, 3, 1, 2, 4)
+        gq, gk, gv = softmax_attention_backward(g(q), g(k), g(v), g(dout), s)
+        for dst, src in ((dq, gq), (dk, gk), (dv, gv)):
+            dst[:, units] = src.transpose(0, 2, 3, 1, 4)
+        return dq, dk, dv
+    for row in units:
+        tok = row[row >= 0]
+        g = lambda x: x[:, tok].transpose(0, 2, 1, 3)
+        gq, gk, gv = softmax_attention_backward(g(q), g(k), g(v), g(dout), s)
+        for dst, src in ((dq, gq), (dk, gk), (dv, gv)):
+            dst[:, tok] = src.transpose(0, 2, 1, 3)
+    return dq, dk, dv
+
+
+def local_pass_backward(q, k, v, dout, grid, tile, scale=None):
+    """Gradients of local_pass (Attn_L) with respect to q, k, v; token order."""
+    q, k, v, dout = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")))
+    s = _default_scale(q.shape[-1], scale)
+    return _units_backward(q, k, v, dout, padded_window_index(grid, tile), s)
+
+
+def global_pass_backward(q, k, v, dout, grid, tile, scale=None):
+    """Gradients of global_pass (Attn_G, value stream v) with respect to q, k, v."""
+    q, k, v, dout = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")))
+    s = _default_scale(q.shape[-1], scale)
+    return _units_backward(q, k, v, dout, padded_window_index(grid, tile).T.copy(), s)
+
+
+def squad_backward(q, k, v, dout, grid, tile, scale=None):
+    """Gradients of squad_forward with respect to q, k and v, given dout.
+
+    out = Attn_G(q, k, o1) with o1 = Attn_L(q, k, v).  q and k enter both passes,
+    so their gradients are the sums of the two passes' gradients; the global
+    pass's value gradient is the upstream gradient of the local output:
+      (dq_G, dk_G, do1) = Attn_G backward at (q, k, o1, dout)
+      (dq_L, dk_L, dv)  = Attn_L backward at (q, k, v, do1)
+      dq = dq_G + dq_L,  dk = dk_G + dk_L.
+    """
+    o1 = local_pass(q, k, v, grid, tile, scale)
+    dq_g, dk_g, do1 = global_pass_backward(q, k, o1, dout, grid, tile, scale)
+    dq_l, dk_l, dv = local_pass_backward(q, k, v, do1, grid, tile, scale)
+    return dq_g + dq_l, dk_g + dk_l, dv
+
+
+def squad_forward_stats(q, k, grid, tile, scale=None):
+    """Per-row softmax statistics of both passes: the natural-log normaliser
+    lse_i = log sum_j exp(scale * <q_i, k_j>) over row i's unit, for the local pass
+    (unit = window) and the global pass (unit = offset group).  Token order
+    [B, n, Hh] each; returns (lse_local, lse_global)."""
+    q = _as_bnhd(q, "q")
+    k = _as_bnhd(k, "k")
+    s = _default_scale(q.shape[-1], scale)
+    out = []
+    for units in (padded_window_index(grid, tile), padded_window_index(grid, tile).T):
+        lse = np.zeros(q.shape[:3])
+        for row in units:
+            tok = row[row >= 0]
+            qu = q[:, tok].transpose(0, 2, 1, 3)        # [B, Hh, L, d]
+            ku = k[:, tok].transpose(0, 2, 1, 3)
+            l = s * np.matmul(qu, np.swapaxes(ku, -1, -2))
+            m = l.max(axis=-1, keepdims=True)
+            lse[:, tok] = (m[..., 0] + np.log(np.exp(l - m).sum(axis=-1))).transpose(0, 2, 1)
+        out.append(lse)
+    return tuple(out)
