@@ -13,7 +13,8 @@ roofline object of the dominant kernel (its average duration from HIP events on
 the launch stream), the float64 CPU oracle timed on a bounded sample of the same
 workload, and a dense full-attention comparator on the 5B-DiT-shaped workload.
 Under `tilings`, the same inputs under the planner's compact tile and on a grid
-cut by the tiling (one column narrower).
+cut by the tiling (one column narrower); under `backward`, the training path
+(forward keeping its statistics, then the gradients) on the same inputs.
 """
 
 import argparse
@@ -41,6 +42,7 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-permutations", action="store_true")
     p.add_argument("--no-tilings", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's timed sample")
     return p.parse_args()
 
@@ -200,6 +202,11 @@ def main():
     if not args.no_permutations:
         perms = permutation_rates(sq, cfg, q, stream)
 
+    backward = None
+    if not args.no_backward:
+        print("[bench] training path (forward_train + backward)", file=sys.stderr, flush=True)
+        backward = backward_rates(sq, cfg, q, k, v, stream)
+
     tilings = None
     if not args.no_tilings and cfg.name == "highres_bf16":
         print("[bench] other tilings of the workload", file=sys.stderr, flush=True)
@@ -244,6 +251,7 @@ def main():
         "dense_comparator": dense,
         "permutations": perms,
         "tilings": tilings,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 
@@ -272,6 +280,37 @@ def permutation_rates(sq, cfg, q, stream):
                      "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del win, grp, tok
     return out
+
+
+def backward_rates(sq, cfg, q, k, v, stream):
+    """The training path on the workload's inputs: squad_attn_forward_train, then
+    squad_attn_backward with a seeded upstream gradient, each timed alone with HIP
+    events.  TFLOP/s counts the standard 2.5x-forward work of a softmax-attention
+    backward (five products of 2 d L flops per row and pass: S, dP, dV, dK, dQ);
+    the kernels compute S and dP twice (once per kind), seven products."""
+    import torch
+
+    g = torch.Generator(device=q.device).manual_seed(77)
+    dout = torch.randn(q.shape, generator=g, device=q.device, dtype=torch.float32).to(q.dtype)
+    out = torch.empty_like(q)
+    ws = torch.empty(sq.squad_attn_train_workspace_size(cfg.grid, cfg.tile, cfg.heads, cfg.batch, cfg.head_dim,
+                                                        cfg.dtype), dtype=torch.uint8, device=q.device)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    fwd = lambda: sq.squad_attn_forward_train(q, k, v, cfg.grid, cfg.tile, cfg.heads, out=out, workspace=ws,
+                                              stream=stream)
+    bwd = lambda: sq.squad_attn_backward(q, k, v, out, dout, cfg.grid, cfg.tile, ws, cfg.heads, dq=grads[0],
+                                         dk=grads[1], dv=grads[2], stream=stream)
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    ms_f = time_launches(fwd, stream, 10)
+    ms_b = time_launches(bwd, stream, 10)
+    rows = cfg.batch * cfg.n * cfg.heads
+    flops = 10.0 * cfg.head_dim * (cfg.window + cfg.windows) * rows
+    del ws, grads, out, dout
+    return {"forward_train_ms": round(ms_f, 4), "backward_ms": round(ms_b, 4),
+            "backward_tflops": round(flops / ms_b / 1e9, 1),
+            "backward_flops": flops, "train_step_ms": round(ms_f + ms_b, 4)}
 
 
 def present_pairs(grid, tile):

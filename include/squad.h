@@ -129,6 +129,50 @@ size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], i
                                  int32_t batch, int32_t head_dim, int32_t dtype);
 
 /*
+ * Training.  The distillation the pages run (flow-matching SFT, then DMD2;
+ * technical summary, "Methodologie") fine-tunes the model through the operator, so
+ * it needs the gradients of out = Attn_G(q, k, Attn_L(q, k, v)).  The pages give no
+ * formula; these entry points compute the chain rule of the two softmax passes:
+ * with o1 = Attn_L(q, k, v) and the upstream gradient dout,
+ *   (dq_G, dk_G, do1) = gradients of Attn_G at (q, k, o1) given dout,
+ *   (dq_L, dk_L, dv)  = gradients of Attn_L at (q, k, v) given do1,
+ *   dq = dq_G + dq_L,  dk = dk_G + dk_L.
+ * Inside one pass, for a unit's softmax P and output o: dv = P^T dout;
+ * dS_ij = P_ij (<dout_i, v_j> - <dout_i, o_i>); dq = scale dS k; dk = scale dS^T q.
+ *
+ * squad_attn_train_workspace_size: bytes of the one workspace both calls take
+ * (the local output, each pass's per-row softmax statistic, and the backward's
+ * scratch: the local output's gradient, per-row <dout, o>, and for bf16 calls
+ * fp32 sums of dq and dk); 0 if the arguments are invalid.
+ *
+ * squad_attn_forward_train: squad_attn_forward (same arguments and checks) that
+ * also keeps, in `workspace`, what squad_attn_backward needs.  `out` is the same
+ * as squad_attn_forward's.
+ *
+ * squad_attn_backward: q, k, v, out (the training forward's output) and dout,
+ * token order [batch, n, heads, head_dim] in `dtype`; writes dq, dk, dv (same
+ * layout and dtype).  `workspace` must hold what squad_attn_forward_train wrote
+ * with the same q, k, v, grid, tile, heads, batch, head_dim, dtype and scale (its
+ * scratch part is overwritten).  bf16 calls compute in fp32 with bf16 MFMA
+ * operands (P and dS rounded to bf16) and round the gradients to bf16 once.
+ * Statuses as for squad_attn_forward; the three outputs must not overlap each
+ * other, an input or the workspace.  Work is enqueued on `stream`: four kernel
+ * launches, no allocation, no synchronisation.
+ */
+size_t squad_attn_train_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                                       int32_t batch, int32_t head_dim, int32_t dtype);
+int squad_attn_forward_train(const void* q, const void* k, const void* v,
+                             const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                             void* out, int32_t batch, int32_t head_dim, int32_t dtype,
+                             float scale, void* workspace, size_t workspace_bytes,
+                             squad_stream_t stream);
+int squad_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const int32_t grid[3], const int32_t tile[3],
+                        int32_t heads, void* dq, void* dk, void* dv, int32_t batch,
+                        int32_t head_dim, int32_t dtype, float scale, void* workspace,
+                        size_t workspace_bytes, squad_stream_t stream);
+
+/*
  * Tile planner.  The pages choose windows of about sqrt(n) tokens (technical
  * summary, "1. SQuad-Attention Operator", Complexiteit: w = sqrt(n) gives
  * O(n sqrt n)).  On a 3-D grid this picks the tile (tt <= T, th <= H, tw <= W)

@@ -31,6 +31,10 @@ __all__ = [
     "squad_window_attn",
     "squad_dense_attn_forward",
     "squad_debug_row_offsets",
+    "squad_attn_train_workspace_size",
+    "squad_attn_forward_train",
+    "squad_attn_backward",
+    "SquadAttention",
     "DTYPE_CODES",
 ]
 
@@ -141,6 +145,68 @@ def _workspace(workspace, need, device):
     if workspace.device != device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     return workspace
+
+
+def squad_attn_train_workspace_size(grid, tile, heads, batch, head_dim, dtype):
+    """Bytes of the workspace squad_attn_forward_train and squad_attn_backward share."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.lib().squad_attn_train_workspace_size(_lib.int3(grid), _lib.int3(tile), int(heads),
+                                                          int(batch), int(head_dim), code))
+
+
+def squad_attn_forward_train(q, k, v, grid, tile, heads=None, out=None, scale=None, workspace=None,
+                             stream=None):
+    """squad_attn_forward that also keeps what the backward needs in the workspace.
+    Returns (out, workspace)."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _out_like(out, q)
+    workspace = _workspace(workspace, squad_attn_train_workspace_size(grid, tile, Hh, B, d, q.dtype), q.device)
+    st = _lib.lib().squad_attn_forward_train(
+        _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(out), B, d,
+        DTYPE_CODES[q.dtype], _scale(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device))
+    _check(st, "squad_attn_forward_train")
+    return out, workspace
+
+
+def squad_attn_backward(q, k, v, out, dout, grid, tile, workspace, heads=None, dq=None, dk=None, dv=None,
+                        scale=None, stream=None):
+    """Gradients (dq, dk, dv) of squad_attn_forward given dout; `workspace` as left by
+    squad_attn_forward_train on the same inputs."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _tensor(out, "out", 4, q.dtype, q.device)
+    dout = _tensor(dout, "dout", 4, q.dtype, q.device)
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    dq, dk, dv = (_out_like(x, q, nm) for x, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    workspace = _workspace(workspace, 0, q.device)
+    st = _lib.lib().squad_attn_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _lib.int3(grid), _lib.int3(tile), Hh,
+        _ptr(dq), _ptr(dk), _ptr(dv), B, d, DTYPE_CODES[q.dtype], _scale(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "squad_attn_backward")
+    return dq, dk, dv
+
+
+class SquadAttention(torch.autograd.Function):
+    """Autograd wrapper: out = SquadAttention.apply(q, k, v, grid, tile[, scale]).
+    The forward keeps the library's training workspace; the backward calls
+    squad_attn_backward (no arithmetic in Python)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, grid, tile, scale=None):
+        q, k, v = (x.contiguous() for x in (q, k, v))
+        out, ws = squad_attn_forward_train(q, k, v, tuple(grid), tuple(tile), scale=scale)
+        ctx.save_for_backward(q, k, v, out, ws)
+        ctx.geom = (tuple(grid), tuple(tile), scale)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, ws = ctx.saved_tensors
+        grid, tile, scale = ctx.geom
+        dq, dk, dv = squad_attn_backward(q, k, v, out, dout.contiguous(), grid, tile, ws, scale=scale)
+        return dq, dk, dv, None, None, None
 
 
 def squad_attn_forward_local(q, k, v, grid, tile, heads=None, scale=None, workspace=None, stream=None):

@@ -33,6 +33,9 @@ EXPORTS = [
     "squad_window_attn",
     "squad_dense_attn_forward",
     "squad_debug_row_offsets",
+    "squad_attn_train_workspace_size",
+    "squad_attn_forward_train",
+    "squad_attn_backward",
 ]
 
 _lib = None
@@ -55,6 +58,12 @@ def _declare(lib):
     lib.squad_attn_forward_global.restype = ctypes.c_int
     lib.squad_attn_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32]
     lib.squad_attn_workspace_size.restype = SZ
+    lib.squad_attn_train_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32]
+    lib.squad_attn_train_workspace_size.restype = SZ
+    lib.squad_attn_forward_train.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, P, SZ, P]
+    lib.squad_attn_forward_train.restype = ctypes.c_int
+    lib.squad_attn_backward.argtypes = [P, P, P, P, P, I3, I3, I32, P, P, P, I32, I32, I32, F, P, SZ, P]
+    lib.squad_attn_backward.restype = ctypes.c_int
     lib.squad_plan_tile.argtypes = [I3, I3]
     lib.squad_plan_tile.restype = ctypes.c_int
     for name in ("squad_local_pass", "squad_global_pass"):

@@ -497,7 +497,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
                      : wave == 2 ? Stage<D, 2>::k() : Stage<D, 0>::v());
   if (NW > 4) ostage = nullptr;  // (only 2- and 4-wave workgroups are launched)
   if (active) {
-    const float inv = 1.f / sum_halves(l_run);
+    const float lsum = sum_halves(l_run);
+    const float inv = 1.f / lsum;
     OT* orow = ostage + l32 * D + 4 * half;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       const uint32_t x = q0 + l32;
       qok = qok && ((rmask[2 * (x >> 5) + ((x >> 2) & 1)] >> (4 * ((x & 31) >> 3) + (x & 3))) & 1);
     }
+    if (a.lse && qok && half == 0) a.lse[(size_t)u * L + q0 + l32] = m_ref + __log2f(lsum);
     const int32_t oo = qok ? a.mo.row_off(q0 + l32) : -1;
 #pragma unroll
     for (int i = 0; i < 32 / WR; ++i) {

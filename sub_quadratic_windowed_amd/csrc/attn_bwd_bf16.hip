@@ -1,0 +1,517 @@
+// attn_bwd_bf16.hip - the 16-bit backward of one SQuad pass (gfx950 MFMA).
+//
+// Gradients of the unit attentions o_i = sum_j P_ij v_j (P_ij = softmax_j of the
+// scaled logits), given the upstream gradient dout:
+//   dv_j = sum_i P_ij dout_i,    dS_ij = P_ij (<dout_i, v_j> - D_i),  D_i = <dout_i, o_i>,
+//   dq_i = scale * sum_j dS_ij k_j,   dk_j = scale * sum_i dS_ij q_i,
+// with P recomputed as exp2(c <q_i, k_j> - lse_i) from the forward's row statistic.
+//
+// Kind A (one query chunk of 32 rows per wave): Q^T and dout^T stay in registers as
+// B operands; per block of 32 keys
+//   S^T  = K * Q^T       (A = K rows from LDS)
+//   dP^T = V * dout^T    (A = V rows from LDS)
+//   dq^T += K^T * dS^T   (A = K^T from LDS with the transposing read, B = dS^T in
+//                         registers: the S^T output layout is the B layout once
+//                         K^T is read with the matching key permutation)
+// so each lane owns one query and its statistics (lse, D) are per-lane scalars.
+// Kind B (one key chunk of 32 rows per wave): K^T and V^T in registers; per block
+// of 32 queries
+//   S  = Q * K^T,  dP = dout * V^T   (A = Q and dout rows from LDS)
+//   dv^T += dout^T * P,  dk^T += Q^T * dS   (A = transposing reads of dout and Q)
+// each lane owning one key; the block's 32 lse and D values sit in LDS.
+//
+// LDS blocks hold 32 rows of 16-bit elements as 8 groups of 4 rows; in group g the
+// 16-byte chunk c of row r sits at slot 4 * (c ^ (g % 4)) + r % 4.  Row reads (A
+// operands, 16 bytes per lane) and transposing reads (ds_read_b64_tr_b16) are
+// then both free of bank conflicts, and a block is filled by direct global -> LDS
+// loads (one 16-byte chunk per lane).  Two stages: the next block is requested
+// before the current one is used.
+//
+// All products are bf16 with fp32 accumulation; fp16 operands (the local output,
+// the global pass's values) are converted to bf16 on the way to the MFMA.  dS and
+// P are rounded to bf16 for their products.
+#include "squad_kernels.h"
+
+namespace squad {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int BN = 32;   // rows per streamed block
+constexpr int NW = 4;    // waves per workgroup
+constexpr int BM = 32 * NW;
+
+template <int D>
+struct BCfg {
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int GRP = 4 * D;             // elements of one 4-row group
+  static constexpr int GPI = 64 / (4 * CPR);    // groups filled by one direct load
+  static constexpr int VINS = BN * CPR / 64;    // direct loads per block
+  static constexpr int VPW = VINS / NW;         // ... per wave
+  static_assert(VPW * NW == VINS && VPW >= 1, "loads split evenly over the waves");
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16(f16x8 x) {
+  bf16x8 y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (__bf16)(float)x[i];
+  return y;
+}
+
+// 8 consecutive 16-bit elements as a bf16 fragment (fp16 storage converted)
+template <bool F16>
+__device__ __forceinline__ bf16x8 frag(uint4 raw) {
+  if constexpr (F16) return to_bf16(__builtin_bit_cast(f16x8, raw));
+  else return __builtin_bit_cast(bf16x8, raw);
+}
+
+template <bool F16>
+__device__ __forceinline__ float elem(const void* p, int i) {
+  if constexpr (F16) return (float)((const _Float16*)p)[i];
+  else return (float)((const __bf16*)p)[i];
+}
+
+// the lane's half of one row's dimensions as B-operand fragments: dims
+// 16 kk + 8 half + (0..7)
+template <int D, bool F16>
+__device__ __forceinline__ void load_row_frags(const void* row, uint32_t half, bf16x8 (&f)[D / 16]) {
+  const char* p = (const char*)row + half * 16;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = frag<F16>(*(const uint4*)(p + kk * 32));
+}
+
+// One LDS block stage: 32 rows x D 16-bit elements in the grouped layout.
+template <int D, int I, int T>
+struct BStage {
+  static __device__ __forceinline__ char* ptr() {
+    __shared__ __attribute__((aligned(1024))) __bf16 buf[BN * D];
+    return (char*)buf;
+  }
+};
+
+// Per-lane geometry of the grouped layout.
+template <int D>
+struct Layout {
+  typedef BCfg<D> C;
+  // direct loads: lane i of load `ins` fills slot i of its groups
+  uint32_t ld_row[C::VPW];      // row within the block
+  uint32_t ld_byte[C::VPW];     // byte offset of the chunk within the row
+  // row reads of chunk 2 kk + half of row l32: byte offset rd[kk % 2] + 256 (kk / 2)
+  // (the swizzle only touches the low two bits of the chunk index)
+  uint32_t rd[2];
+  // transposing reads (lo: groups 4 jk + half, hi: + 2): byte offsets within a block
+  uint32_t tr_lo, tr_hi;
+
+  __device__ __forceinline__ void init(uint32_t lane, uint32_t wave) {
+    const uint32_t half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const uint32_t ins = wave + i * NW;
+      const uint32_t g = ins * C::GPI + lane / (4 * C::CPR);
+      const uint32_t slot = lane % (4 * C::CPR);
+      ld_row[i] = 4 * g + (slot & 3);
+      ld_byte[i] = (((slot >> 2) ^ (g & 3)) << 4);
+    }
+    const uint32_t g = l32 >> 2, rr = l32 & 3;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      rd[kk] = 2 * (g * C::GRP + (4 * ((2 * kk + half) ^ (g & 3)) + rr) * 8);
+    const uint32_t tdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const uint32_t rowq = (lane & 15) >> 2;
+    const uint32_t glo = half, ghi = half + 2;
+    tr_lo = 2 * (glo * C::GRP + 8 * (4 * ((tdim >> 3) ^ glo) + rowq) + (tdim & 7));
+    tr_hi = 2 * (ghi * C::GRP + 8 * (4 * ((tdim >> 3) ^ ghi) + rowq) + (tdim & 7));
+  }
+};
+
+// A operand from rows: 32 rows x dims 16 kk ... (lane: row l32, chunk 2 kk + half)
+template <int D, bool F16>
+__device__ __forceinline__ bf16x8 read_rows(const char* stage, const Layout<D>& lay, int kk) {
+  return frag<F16>(*(const uint4*)(stage + lay.rd[kk & 1] + 256 * (kk >> 1)));
+}
+
+// A operand transposed: dims 32 mt + (lane % 32) x rows 16 jk + (permuted)
+template <int D, bool F16>
+__device__ __forceinline__ bf16x8 read_tr(const char* stage, const Layout<D>& lay, int jk, int mt) {
+  typedef BCfg<D> C;
+  const char* p = stage + 2 * (4 * jk * C::GRP + 128 * mt);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p + lay.tr_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p + lay.tr_hi));
+  uint4 raw;
+  raw.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  raw.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  raw.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  raw.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return frag<F16>(raw);
+}
+
+struct UnitPos {
+  uint32_t u, s, b, h, chunk;
+};
+__device__ __forceinline__ bool unit_pos(const BwdArgs& a, UnitPos& p) {
+  const uint32_t wg = blockIdx.x;
+  const uint32_t jj = wg >> 3;
+  p.chunk = jj % a.nchunks;
+  p.u = (jj / a.nchunks) * 8 + (wg & 7);
+  if (p.u >= a.units) return false;
+  p.s = a.fBH.div(p.u);
+  const uint32_t bh = p.u - p.s * a.BH;
+  p.b = a.fHeads.div(bh);
+  p.h = bh - p.b * a.heads;
+  return true;
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Store a transposed accumulator tile set (element (dim 32 mt + 8 (r/4) + 4 half +
+// r % 4) of this lane's row) as fp32 (accumulate or plain) or bf16.
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float scale, uint32_t half,
+                                           bool final_pass, float* accp, __bf16* outp) {
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * mt + 8 * g + 4 * half;
+      float4 x = make_float4(acc[mt][4 * g] * scale, acc[mt][4 * g + 1] * scale, acc[mt][4 * g + 2] * scale,
+                             acc[mt][4 * g + 3] * scale);
+      if (final_pass) {
+        if (accp) {
+          const float4 y = *(const float4*)(accp + d0);
+          x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        }
+        bf16x4 w;
+        w[0] = (__bf16)x.x; w[1] = (__bf16)x.y; w[2] = (__bf16)x.z; w[3] = (__bf16)x.w;
+        *(bf16x4*)(outp + d0) = w;
+      } else {
+        *(float4*)(accp + d0) = x;
+      }
+    }
+}
+
+// ---------------------------------------------------------------- kind A: dq (and D)
+
+template <int D, bool VF16, bool OF16, bool CUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(BwdArgs a) {
+  typedef BCfg<D> C;
+  UnitPos p;
+  if (!unit_pos(a, p)) return;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t half = lane >> 5, l32 = lane & 31;
+  const uint32_t L = a.L;
+  UnitDigits ud;
+  if constexpr (CUT) ud = cut_unit_digits(a, p.s);
+  auto present = [&](uint32_t r) -> bool {
+    if constexpr (CUT) return r < L && cut_present(a, ud, r);
+    return r < L;
+  };
+  // the row a load of row r reads: r itself, or a present row standing in for it
+  auto load_row = [&](uint32_t r) -> uint32_t {
+    if constexpr (CUT) return present(r) ? r : 0;
+    return min(r, L - 1);
+  };
+  const char* qg = (const char*)a.q + 2 * a.mqk.base(p.b, p.h, p.s);
+  const char* kg = (const char*)a.k + 2 * a.mqk.base(p.b, p.h, p.s);
+  const char* vg = (const char*)a.v + 2 * a.mv.base(p.b, p.h, p.s);
+  const char* og = (const char*)a.o + 2 * a.mo.base(p.b, p.h, p.s);
+  const char* dg = (const char*)a.dout + 2 * a.mdo.base(p.b, p.h, p.s);
+
+  const uint32_t q0 = p.chunk * BM + wave * 32;
+  const bool active = q0 < L;
+  const uint32_t qi = q0 + l32;
+  const bool qok = present(qi);
+  const uint32_t qr = load_row(qi);
+
+  // query and upstream-gradient fragments; D = <dout, o> over this lane's dims
+  bf16x8 qf[D / 16], df[D / 16];
+  load_row_frags<D, false>(qg + 2 * a.mqk.row_off(qr), half, qf);
+  load_row_frags<D, false>(dg + 2 * a.mdo.row_off(qr), half, df);
+  float dsum = 0.f;
+  {
+    const char* orow = og + 2 * a.mo.row_off(qr) + half * 16;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const uint4 raw = *(const uint4*)(orow + kk * 32);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)df[kk][e], elem<OF16>(&raw, e), dsum);
+    }
+  }
+  dsum = sum_halves(dsum);
+  const size_t row_id = (size_t)p.u * L + qi;
+  const float lse = qok ? a.lse[row_id] : 0.f;
+  if (qok && half == 0) a.dsum[row_id] = dsum;
+
+  Layout<D> lay;
+  lay.init(lane, wave);
+  const uint32_t nkb = (L + BN - 1) / BN;
+  auto issue = [&](uint32_t kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    char* ks = BStage<D, ST, 0>::ptr();
+    char* vs = BStage<D, ST, 1>::ptr();
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const uint32_t ins = wave + i * NW;
+      const uint32_t r = load_row(kb * BN + lay.ld_row[i]);
+      __builtin_amdgcn_global_load_lds((const void*)(kg + 2 * a.mqk.row_off(r) + lay.ld_byte[i]),
+                                       (lds_void_t*)(ks + ins * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg + 2 * a.mv.row_off(r) + lay.ld_byte[i]),
+                                       (lds_void_t*)(vs + ins * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+  const float c = a.c;
+
+  auto step = [&](uint32_t kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    if (kb + 1 < nkb) issue(kb + 1, std::integral_constant<int, ST ^ 1>{});
+    if (active) {
+      const char* ks = BStage<D, ST, 0>::ptr();
+      const char* vs = BStage<D, ST, 1>::ptr();
+      f32x16 sc, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        sc = mfma(read_rows<D, false>(ks, lay, kk), qf[kk], sc);
+        dp = mfma(read_rows<D, VF16>(vs, lay, kk), df[kk], dp);
+      }
+      // present keys of the block: bit j for key kb * 32 + j, then this half's bits
+      uint32_t km = 0xffffffffu;
+      if constexpr (CUT) {
+        km = (uint32_t)__ballot(present(kb * BN + l32));
+      } else if ((kb + 1) * BN > L) {
+        km = (1u << (L - kb * BN)) - 1u;   // fewer than 32 keys left
+      }
+      km >>= 4 * half;
+      bf16x8 db[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pij = ((km >> (8 * (r / 4) + (r % 4))) & 1) ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse)) : 0.f;
+        db[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dsum));
+      }
+#pragma unroll
+      for (int jk = 0; jk < 2; ++jk)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma(read_tr<D, false>(ks, lay, jk, mt), db[jk], acc[mt]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  issue(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    step(kb, std::integral_constant<int, 0>{});
+    step(kb + 1, std::integral_constant<int, 1>{});
+  }
+  if (kb < nkb) step(kb, std::integral_constant<int, 0>{});
+
+  if (active && qok) {
+    const int64_t base = a.mdq.base(p.b, p.h, p.s) + a.mdq.row_off(qi);
+    store_rows<D>(acc, a.scale, half, a.final_pass != 0, a.dq_acc + base,
+                  a.final_pass ? (__bf16*)a.dq + base : nullptr);
+  }
+}
+
+// ---------------------------------------------------------------- kind B: dk, dv
+
+template <int D, bool VF16, bool CUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(BwdArgs a) {
+  typedef BCfg<D> C;
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BN], dsum_s[2][BN];
+  UnitPos p;
+  if (!unit_pos(a, p)) return;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t half = lane >> 5, l32 = lane & 31;
+  const uint32_t L = a.L;
+  UnitDigits ud;
+  if constexpr (CUT) ud = cut_unit_digits(a, p.s);
+  auto present = [&](uint32_t r) -> bool {
+    if constexpr (CUT) return r < L && cut_present(a, ud, r);
+    return r < L;
+  };
+  auto load_row = [&](uint32_t r) -> uint32_t {
+    if constexpr (CUT) return present(r) ? r : 0;
+    return min(r, L - 1);
+  };
+  const char* qg = (const char*)a.q + 2 * a.mqk.base(p.b, p.h, p.s);
+  const char* kg = (const char*)a.k + 2 * a.mqk.base(p.b, p.h, p.s);
+  const char* vg = (const char*)a.v + 2 * a.mv.base(p.b, p.h, p.s);
+  const char* dg = (const char*)a.dout + 2 * a.mdo.base(p.b, p.h, p.s);
+
+  const uint32_t k0 = p.chunk * BM + wave * 32;
+  const bool active = k0 < L;
+  const uint32_t kj = k0 + l32;
+  const bool kok = present(kj);
+  const uint32_t kr = load_row(kj);
+  bf16x8 kf[D / 16];
+  load_row_frags<D, false>(kg + 2 * a.mqk.row_off(kr), half, kf);
+  // the workgroup's own V rows, bf16, in LDS: chunk c of row r at slot c ^ (r % CPR)
+  // (read as the B operand of dP, one 16-byte chunk per lane, conflict-free);
+  // holding them in registers instead would not leave room for both accumulators
+  __shared__ __attribute__((aligned(1024))) __bf16 vown[BM * D];
+  {
+    constexpr int PER = BM * C::CPR / 256;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t ch = tid + 256 * i;
+      const uint32_t r = ch / C::CPR, cc = ch % C::CPR;
+      const uint32_t vr = load_row(p.chunk * BM + r);
+      const uint4 raw = *(const uint4*)(vg + 2 * a.mv.row_off(vr) + 16 * cc);
+      *(bf16x8*)((char*)vown + r * D * 2 + ((cc ^ (r & (C::CPR - 1))) << 4)) = frag<VF16>(raw);
+    }
+  }
+  const char* vrow_lds = (const char*)vown + (wave * 32 + l32) * D * 2;
+  const uint32_t vxor = l32 & (C::CPR - 1);
+
+  Layout<D> lay;
+  lay.init(lane, wave);
+  const size_t unit_rows = (size_t)p.u * L;
+  const uint32_t nqb = (L + BN - 1) / BN;
+  auto issue = [&](uint32_t qb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    char* qs = BStage<D, ST, 2>::ptr();
+    char* ds = BStage<D, ST, 3>::ptr();
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const uint32_t ins = wave + i * NW;
+      const uint32_t r = load_row(qb * BN + lay.ld_row[i]);
+      __builtin_amdgcn_global_load_lds((const void*)(qg + 2 * a.mqk.row_off(r) + lay.ld_byte[i]),
+                                       (lds_void_t*)(qs + ins * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(dg + 2 * a.mdo.row_off(r) + lay.ld_byte[i]),
+                                       (lds_void_t*)(ds + ins * 1024), 16, 0, 0);
+    }
+    // the block's row statistics (absent rows: lse = +inf, so their weights are 0)
+    if (wave == 0 && lane < BN) {
+      const uint32_t r = qb * BN + lane;
+      const bool ok = present(r);
+      lse_s[ST][lane] = ok ? a.lse[unit_rows + r] : INFINITY;
+      dsum_s[ST][lane] = ok ? a.dsum[unit_rows + r] : 0.f;
+    }
+  };
+
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dka[mt][r] = 0.f; dva[mt][r] = 0.f; }
+  const float c = a.c;
+
+  auto step = [&](uint32_t qb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    if (qb + 1 < nqb) issue(qb + 1, std::integral_constant<int, ST ^ 1>{});
+    if (active) {
+      const char* qs = BStage<D, ST, 2>::ptr();
+      const char* ds = BStage<D, ST, 3>::ptr();
+      f32x16 sc, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        sc = mfma(read_rows<D, false>(qs, lay, kk), kf[kk], sc);
+        dp = mfma(read_rows<D, false>(ds, lay, kk),
+                  *(const bf16x8*)(vrow_lds + (((uint32_t)(2 * kk) + half) ^ vxor) * 16), dp);
+      }
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // queries 8 g + 4 half + (0..3) of the block
+        const float4 ls = *(const float4*)&lse_s[ST][8 * g + 4 * half];
+        const float4 dd = *(const float4*)&dsum_s[ST][8 * g + 4 * half];
+        const float lv[4] = {ls.x, ls.y, ls.z, ls.w};
+        const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pij = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e]));
+          pb[r / 8][r % 8] = (__bf16)pij;
+          sb[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dv4[e]));
+        }
+      }
+#pragma unroll
+      for (int jk = 0; jk < 2; ++jk)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+          dva[mt] = mfma(read_tr<D, false>(ds, lay, jk, mt), pb[jk], dva[mt]);
+          dka[mt] = mfma(read_tr<D, false>(qs, lay, jk, mt), sb[jk], dka[mt]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  issue(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t qb = 0;
+  for (; qb + 2 <= nqb; qb += 2) {
+    step(qb, std::integral_constant<int, 0>{});
+    step(qb + 1, std::integral_constant<int, 1>{});
+  }
+  if (qb < nqb) step(qb, std::integral_constant<int, 0>{});
+
+  if (active && kok) {
+    const int64_t kbase = a.mdk.base(p.b, p.h, p.s) + a.mdk.row_off(kj);
+    store_rows<D>(dka, a.scale, half, a.final_pass != 0, a.dk_acc + kbase,
+                  a.final_pass ? (__bf16*)a.dk + kbase : nullptr);
+    const int64_t vbase = a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(kj);
+    store_rows<D>(dva, 1.f, half, true, nullptr, (__bf16*)a.dv + vbase);
+  }
+}
+
+template <int D, bool VF16, bool OF16>
+hipError_t launch(const BwdArgs& a, bool kind_b, hipStream_t stream) {
+  const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  const dim3 grid((uint32_t)blocks), block(64 * NW);
+  if (kind_b) {
+    if (a.cut.on) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false>), grid, block, 0, stream, a);
+  } else {
+    if (a.cut.on) hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_types(const BwdArgs& a, BwdTypes t, bool kind_b, hipStream_t stream) {
+  if (t.v_f16 && !t.o_f16) return launch<D, true, false>(a, kind_b, stream);
+  if (!t.v_f16 && t.o_f16) return launch<D, false, true>(a, kind_b, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hipStream_t stream) {
+  a.nchunks = (a.L + BM - 1) / BM;
+  if (head_dim == 128) return launch_types<128>(a, t, kind_b, stream);
+  if (head_dim == 64) return launch_types<64>(a, t, kind_b, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace squad

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 
   if (qok) {
+    if (a.lse && part == 0) a.lse[(size_t)u * L + qi] = m_run + __log2f(l_run);
     const float inv = 1.f / l_run;
     float* orow = og + a.mo.row_off(qi) + part * DL;
 #pragma unroll

@@ -251,7 +251,8 @@ int check_forward(const void* const* in, int nin, const void* out, const int32_t
 // Cut tilings: a row is present iff its token lies inside the grid.  Token
 // coordinate on each axis = window digit * tile size + offset digit; the local
 // pass's units are windows (rows offsets), the global pass's the reverse.
-void set_cut(AttnArgs& a, const Geo& g, bool by_window) {
+template <typename Args>
+void set_cut(Args& a, const Geo& g, bool by_window) {
   if (!g.cut) return;
   a.cut.on = 1;
   a.cut.lim[0] = (uint32_t)g.T; a.cut.lim[1] = (uint32_t)g.H; a.cut.lim[2] = (uint32_t)g.W;
@@ -266,8 +267,10 @@ void set_cut(AttnArgs& a, const Geo& g, bool by_window) {
 // workspace, group-major.  bf16: held as fp16 between the passes (its bf16 rounding
 // would take about half of the 1.5e-2 error budget; fp16 costs the same bytes).
 int forward_local(const void* q, const void* k, const void* v, const Geo& g, int32_t heads, int32_t batch,
-                  int32_t head_dim, int32_t dtype, float scale, void* workspace, hipStream_t s) {
+                  int32_t head_dim, int32_t dtype, float scale, void* workspace, hipStream_t s,
+                  float* lse = nullptr) {
   AttnArgs a = attn_args(q, k, v, workspace, (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, scale);
+  a.lse = lse;
   a.mqk = token_map(g, heads, head_dim, true);
   a.mv = a.mqk;
   a.mo = group_major_map(g, heads, head_dim, true);
@@ -278,13 +281,71 @@ int forward_local(const void* q, const void* k, const void* v, const Geo& g, int
 // Global pass of the forward: units = offset groups, rows = windows; the value
 // stream is the local output in the workspace; the output goes to token order.
 int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_t heads, int32_t batch,
-                   int32_t head_dim, int32_t dtype, float scale, const void* workspace, hipStream_t s) {
+                   int32_t head_dim, int32_t dtype, float scale, const void* workspace, hipStream_t s,
+                   float* lse = nullptr) {
   AttnArgs a = attn_args(q, k, workspace, out, (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, scale);
+  a.lse = lse;
   a.mqk = token_map(g, heads, head_dim, false);
   a.mv = group_major_map(g, heads, head_dim, false);
   a.mo = a.mqk;
   set_cut(a, g, false);
   return run_attn(a, head_dim, dtype, s, VType::kF16ToBf16);
+}
+
+// ---- training: the forward's saved state and the backward's scratch, in one
+// workspace (sections 256-byte aligned)
+struct TrainLayout {
+  size_t o1, lse_l, lse_g, dsum, do1, dq_acc, dk_acc, total;
+};
+
+TrainLayout train_layout(const Geo& g, int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t bh = (size_t)heads * (size_t)batch;
+  const size_t cells = (size_t)g.G * (size_t)g.Wn;   // rows of one pass per (batch, head)
+  const size_t esz = elem_bytes(dtype);
+  TrainLayout t;
+  t.o1 = 0;
+  t.lse_l = al(t.o1 + bh * cells * head_dim * esz);
+  t.lse_g = al(t.lse_l + bh * cells * 4);
+  t.dsum = al(t.lse_g + bh * cells * 4);
+  t.do1 = al(t.dsum + bh * cells * 4);
+  size_t end = al(t.do1 + bh * cells * head_dim * esz);
+  // bf16 calls sum dq and dk over the passes in fp32 (fp32 calls use dq and dk)
+  t.dq_acc = t.dk_acc = 0;
+  if (dtype == SQUAD_DTYPE_BF16) {
+    t.dq_acc = end;
+    t.dk_acc = al(t.dq_acc + bh * (size_t)g.n * head_dim * 4);
+    end = al(t.dk_acc + bh * (size_t)g.n * head_dim * 4);
+  }
+  t.total = end;
+  return t;
+}
+
+BwdArgs bwd_args(const Geo& g, bool local, int32_t heads, int32_t batch, int32_t head_dim, float scale) {
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.L = (uint32_t)(local ? g.Wn : g.G);
+  a.U = (uint32_t)(local ? g.G : g.Wn);
+  a.heads = (uint32_t)heads;
+  a.BH = (uint32_t)(heads * batch);
+  a.fBH = FastDiv(a.BH);
+  a.fHeads = FastDiv(a.heads);
+  a.units = a.BH * a.U;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)head_dim);
+  a.scale = (float)sc;
+  a.c = (float)(sc * 1.4426950408889634);
+  set_cut(a, g, local);
+  return a;
+}
+
+int run_bwd(const BwdArgs& a, int32_t head_dim, int32_t dtype, BwdTypes t, hipStream_t s) {
+  if (a.units == 0 || a.L == 0) return SQUAD_OK;
+  for (int kind = 0; kind < 2; ++kind) {
+    const hipError_t e = dtype == SQUAD_DTYPE_BF16 ? launch_bwd_bf16(a, head_dim, t, kind == 1, s)
+                                                   : launch_bwd_f32(a, head_dim, kind == 1, s);
+    if (e != hipSuccess) return SQUAD_ERR_HIP;
+  }
+  return SQUAD_OK;
 }
 
 }  // namespace
@@ -541,6 +602,112 @@ int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t 
           offsets[i++] = (!a.cut.on || cut_present(a, ud, r)) ? base + m.row_off(r) : -1;
       }
   return SQUAD_OK;
+}
+
+// ---- training forward and backward
+
+size_t squad_attn_train_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                                       int32_t batch, int32_t head_dim, int32_t dtype) {
+  Geo g;
+  size_t bytes = 0;
+  if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true)) return 0;
+  return train_layout(g, heads, batch, head_dim, dtype).total;
+}
+
+int squad_attn_forward_train(const void* q, const void* k, const void* v, const int32_t grid[3],
+                             const int32_t tile[3], int32_t heads, void* out, int32_t batch,
+                             int32_t head_dim, int32_t dtype, float scale, void* workspace,
+                             size_t workspace_bytes, squad_stream_t stream) {
+  Geo g;
+  if (!out) return SQUAD_ERR_INVALID_ARG;
+  const void* in[3] = {q, k, v};
+  int st = check_forward(in, 3, out, grid, tile, heads, batch, head_dim, dtype, scale, workspace,
+                         workspace_bytes, g);
+  if (st) return st;
+  const TrainLayout t = train_layout(g, heads, batch, head_dim, dtype);
+  if (workspace_bytes < t.total) return SQUAD_ERR_WORKSPACE;
+  size_t bytes = (size_t)heads * batch * g.n * head_dim * elem_bytes(dtype);
+  for (int i = 0; i < 3; ++i)
+    if (overlap(in[i], bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  if (overlap(out, bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  st = forward_local(q, k, v, g, heads, batch, head_dim, dtype, scale, ws + t.o1, s, (float*)(ws + t.lse_l));
+  if (st) return st;
+  return forward_global(q, k, out, g, heads, batch, head_dim, dtype, scale, ws + t.o1, s,
+                        (float*)(ws + t.lse_g));
+}
+
+int squad_attn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const int32_t grid[3], const int32_t tile[3], int32_t heads, void* dq, void* dk,
+                        void* dv, int32_t batch, int32_t head_dim, int32_t dtype, float scale,
+                        void* workspace, size_t workspace_bytes, squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true);
+  if (st) return st;
+  const void* in[5] = {q, k, v, out, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (const void* p : in)
+    if (!p) return SQUAD_ERR_INVALID_ARG;
+  for (const void* p : outs)
+    if (!p) return SQUAD_ERR_INVALID_ARG;
+  if (!workspace) return SQUAD_ERR_WORKSPACE;
+  for (const void* p : in)
+    if (misaligned(p)) return SQUAD_ERR_ALIGN;
+  for (const void* p : outs)
+    if (misaligned(p)) return SQUAD_ERR_ALIGN;
+  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
+  const TrainLayout t = train_layout(g, heads, batch, head_dim, dtype);
+  if (workspace_bytes < t.total) return SQUAD_ERR_WORKSPACE;
+  for (int i = 0; i < 3; ++i) {
+    for (const void* p : in)
+      if (overlap(outs[i], bytes, p, bytes)) return SQUAD_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], bytes, outs[j], bytes)) return SQUAD_ERR_ALIAS;
+    if (overlap(outs[i], bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  }
+  for (const void* p : in)
+    if (overlap(p, bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == SQUAD_DTYPE_BF16;
+  float* dq_acc = bf16 ? (float*)(ws + t.dq_acc) : (float*)dq;
+  float* dk_acc = bf16 ? (float*)(ws + t.dk_acc) : (float*)dk;
+
+  // global pass: units = offset groups, values = the local output; its value
+  // gradient (the local output's gradient) goes to the workspace, group-major
+  BwdArgs ag = bwd_args(g, false, heads, batch, head_dim, scale);
+  ag.q = q; ag.k = k; ag.v = ws + t.o1; ag.o = out; ag.dout = dout;
+  ag.mqk = token_map(g, heads, head_dim, false);
+  ag.mv = group_major_map(g, heads, head_dim, false);
+  ag.mo = ag.mqk; ag.mdo = ag.mqk;
+  ag.lse = (const float*)(ws + t.lse_g);
+  ag.dsum = (float*)(ws + t.dsum);
+  ag.dq_acc = dq_acc; ag.dk_acc = dk_acc;
+  ag.mdq = ag.mqk; ag.mdk = ag.mqk;
+  ag.dv = ws + t.do1; ag.mdv = ag.mv;
+  ag.final_pass = 0;
+  st = run_bwd(ag, head_dim, dtype, BwdTypes{true, false}, s);
+  if (st) return st;
+
+  // local pass: units = windows, upstream gradient = the local output's gradient;
+  // adds the global pass's dq and dk and writes the three gradients
+  BwdArgs al = bwd_args(g, true, heads, batch, head_dim, scale);
+  al.q = q; al.k = k; al.v = v; al.o = ws + t.o1; al.dout = ws + t.do1;
+  al.mqk = token_map(g, heads, head_dim, true);
+  al.mv = al.mqk;
+  al.mo = group_major_map(g, heads, head_dim, true);
+  al.mdo = al.mo;
+  al.lse = (const float*)(ws + t.lse_l);
+  al.dsum = (float*)(ws + t.dsum);
+  al.dq = dq; al.dk = dk; al.dq_acc = dq_acc; al.dk_acc = dk_acc;
+  al.mdq = al.mqk; al.mdk = al.mqk;
+  al.dv = dv; al.mdv = al.mqk;
+  al.final_pass = 1;
+  return run_bwd(al, head_dim, dtype, BwdTypes{false, true}, s);
 }
 
 }  // extern "C"

@@ -41,19 +41,22 @@ struct AttnArgs {
   uint32_t v_like_k; // nonzero: mv locates rows exactly as mqk does
   float c;           // softmax scale * log2(e)
   Cut cut;           // absent rows (cut tilings only; on == 0 otherwise)
+  float* lse;        // optional: row statistics lse[u * L + r] = log2 sum_j exp2(c <q_r, k_j>)
 };
 
 // The digits of unit s under the token map, for Cut tests of its rows.
 struct UnitDigits {
   uint32_t d[3];
 };
-__host__ __device__ __forceinline__ UnitDigits cut_unit_digits(const AttnArgs& a, uint32_t s) {
+template <typename Args>
+__host__ __device__ __forceinline__ UnitDigits cut_unit_digits(const Args& a, uint32_t s) {
   UnitDigits u;
   a.mqk.unit.digits(s, u.d[0], u.d[1], u.d[2]);
   return u;
 }
 // Whether row r (< L) of the unit is a token of the grid.
-__host__ __device__ __forceinline__ bool cut_present(const AttnArgs& a, const UnitDigits& u, uint32_t r) {
+template <typename Args>
+__host__ __device__ __forceinline__ bool cut_present(const Args& a, const UnitDigits& u, uint32_t r) {
   uint32_t r2, r1, r0;
   a.mqk.row.digits(r, r2, r1, r0);
   return u.d[0] * a.cut.su[0] + r2 * a.cut.sr[0] < a.cut.lim[0] &&
@@ -68,6 +71,49 @@ enum class VType { kBf16ToBf16, kBf16ToF16, kF16ToBf16 };
 
 hipError_t launch_attn_bf16(AttnArgs a, int head_dim, VType vtype, hipStream_t stream);
 hipError_t launch_attn_f32(AttnArgs a, int head_dim, hipStream_t stream);
+
+// Backward of one pass (the gradients of the unit attentions above), in two
+// launches over the same units and rows:
+//   kind A (per query row i):  D_i = <dout_i, o_i>;  dq_i = scale * sum_j dS_ij k_j
+//   kind B (per key row j):    dv_j = sum_i P_ij dout_i;  dk_j = scale * sum_i dS_ij q_i
+// with P_ij = exp2(c <q_i, k_j> - lse_i) and dS_ij = P_ij (<dout_i, v_j> - D_i).
+// Kind A writes D (dsum) for kind B.  dq and dk are summed over the two passes:
+// the first pass writes its part to the fp32 accumulators (token order, the
+// offsets of mdq / mdk); the second adds them and writes dq / dk in the call's
+// dtype (for fp32 calls the accumulators may be dq and dk themselves).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;      // value rows (the global pass: the local output)
+  const void* o;      // this pass's output rows (kind A, for D)
+  const void* dout;   // upstream gradient of this pass's output
+  RowMap mqk, mv, mo, mdo;
+  const float* lse;   // [u * L + r]
+  float* dsum;        // [u * L + r]: D, written by kind A, read by kind B
+  void* dq;           // kind A, final pass: dq in the call's dtype (token order, mdq)
+  void* dk;           // kind B, final pass: dk
+  float* dq_acc;      // fp32 accumulators (mdq / mdk offsets)
+  float* dk_acc;
+  void* dv;           // kind B: value gradient rows (mdv)
+  RowMap mdq, mdk, mdv;
+  uint32_t final_pass;  // 0: write the accumulators; 1: add them, write dq / dk
+  uint32_t L, U, heads, BH;
+  FastDiv fBH, fHeads;
+  uint32_t units, nchunks;
+  float c;            // softmax scale * log2(e)
+  float scale;
+  Cut cut;
+};
+
+// Element types of the bf16 engine's backward launches (q, k, dout and the
+// gradients are bf16; o and v may be the fp16 local output).
+struct BwdTypes {
+  bool v_f16;         // value rows are fp16 (the global pass: the local output)
+  bool o_f16;         // output rows are fp16 (the local pass: the local output)
+};
+
+hipError_t launch_bwd_f32(BwdArgs a, int head_dim, bool kind_b, hipStream_t stream);
+hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hipStream_t stream);
 
 // Row-permutation copy: rows e = (bh * U + s) * L + r for bh < BH, s < U, r < L;
 // row e is read at src + ms(b, h, s, r) and written at dst + md(b, h, s, r).
