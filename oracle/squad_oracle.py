@@ -50,6 +50,12 @@ through the operator.  q and k receive the sum of both passes' gradients; the
 global pass's value gradient is the upstream gradient of the local output.
 squad_forward_stats gives each row's softmax normaliser (log-sum-exp) per pass.
 
+More than two passes (squad_kpass_forward): the pages name composing more than
+two passes as future work.  The reading taken: nested tiles t1 | t2 | ... | grid
+split each axis coordinate into k digits; pass j attends among the tokens that
+differ only in digit j, and each pass's output is the next pass's value stream.
+k = 2 is the operator above.
+
 All arithmetic is float64.  Every function below is written from the definition,
 with numpy fancy indexing and numpy matmul as its only library steps.
 """
@@ -77,6 +83,8 @@ __all__ = [
     "global_pass_backward",
     "squad_backward",
     "squad_forward_stats",
+    "kpass_level_index",
+    "squad_kpass_forward",
 ]
 
 
@@ -402,3 +410,69 @@ def squad_forward_stats(q, k, grid, tile, scale=None):
             lse[:, tok] = (m[..., 0] + np.log(np.exp(l - m).sum(axis=-1))).transpose(0, 2, 1)
         out.append(lse)
     return tuple(out)
+
+
+# ---- more than two passes (the pages name composing more than two passes as
+# future work, to trade depth for efficiency; technical summary, "Beperkingen en
+# Conclusie") ----
+
+def _kpass_levels(grid, tiles):
+    """Per-axis level sizes of a nested tiling: tiles[0] | tiles[1] | ... | grid."""
+    T, H, W = (int(x) for x in grid)
+    ext = [(1, 1, 1)] + [tuple(int(x) for x in t) for t in tiles] + [(T, H, W)]
+    for a, b in zip(ext[:-1], ext[1:]):
+        for x, y in zip(a, b):
+            if x <= 0 or y % x:
+                raise ValueError(f"tiles {tiles} are not nested in grid {grid}")
+    return ext
+
+
+def kpass_level_index(grid, tiles, level):
+    """Units of pass `level` (0-based) of the k-pass operator: int64 idx[U, L].
+
+    With nested tiles t1 | t2 | ... | t(k-1) | grid, a token's coordinate on each
+    axis splits into k digits: digit j is its position among the t(j)-tiles inside
+    its t(j+1)-tile (t0 = 1 cell, tk = the grid).  Pass j mixes the tokens that
+    agree on every digit except digit j: row r of idx lists the L tokens of one
+    unit, ordered by their level-j digits row-major over (t, h, w); units run over
+    the other digits.  k = 2 gives the local pass (level 0, units = windows) and
+    the global pass (level 1, units = offsets).
+    """
+    ext = _kpass_levels(grid, tiles)
+    T, H, W = (int(x) for x in grid)
+    k = len(ext) - 1
+    coords = np.stack(np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij"), -1).reshape(-1, 3)
+    tok = (coords[:, 0] * H + coords[:, 1]) * W + coords[:, 2]
+    # digit j on axis a: (x // ext[j][a]) % (ext[j+1][a] // ext[j][a])
+    digits = [np.stack([(coords[:, a] // ext[j][a]) % (ext[j + 1][a] // ext[j][a]) for a in range(3)], -1)
+              for j in range(k)]
+    radix = [tuple(ext[j + 1][a] // ext[j][a] for a in range(3)) for j in range(k)]
+    row = (digits[level][:, 0] * radix[level][1] + digits[level][:, 1]) * radix[level][2] + digits[level][:, 2]
+    unit = np.zeros(len(tok), dtype=np.int64)
+    for j in range(k):
+        if j == level:
+            continue
+        d = digits[j]
+        unit = ((unit * radix[j][0] + d[:, 0]) * radix[j][1] + d[:, 1]) * radix[j][2] + d[:, 2]
+    L = int(np.prod(radix[level]))
+    idx = np.empty((len(tok) // L, L), dtype=np.int64)
+    idx[unit, row] = tok
+    return idx
+
+
+def squad_kpass_forward(q, k, v, grid, tiles, scale=None):
+    """The operator with k = len(tiles) + 1 composed passes: o_0 = v and
+    o_(j+1) = pass j (q, k, o_j), each pass the standard softmax attention inside
+    its units (kpass_level_index); the output is o_k.  Same q and k in every pass,
+    as in the two-pass operator, of which this is the k-level form (k = 2: tiles =
+    [tile])."""
+    q, k, v = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v")))
+    s = _default_scale(q.shape[-1], scale)
+    o = v
+    for level in range(len(tiles) + 1):
+        idx = kpass_level_index(grid, tiles, level)
+        g = lambda x: x[:, idx].transpose(0, 3, 1, 2, 4)    # [B, Hh, U, L, d]
+        ou = softmax_attention(g(q), g(k), g(o), s)
+        o = np.empty_like(v)
+        o[:, idx] = ou.transpose(0, 2, 3, 1, 4)
+    return o
