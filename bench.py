@@ -14,7 +14,8 @@ the launch stream), the float64 CPU oracle timed on a bounded sample of the same
 workload, and a dense full-attention comparator on the 5B-DiT-shaped workload.
 Under `tilings`, the same inputs under the planner's compact tile and on a grid
 cut by the tiling (one column narrower); under `backward`, the training path
-(forward keeping its statistics, then the gradients) on the same inputs.
+(forward keeping its statistics, then the gradients) on the same inputs; under
+`kpass`, the three-level operator on the same inputs.
 """
 
 import argparse
@@ -207,6 +208,11 @@ def main():
         print("[bench] training path (forward_train + backward)", file=sys.stderr, flush=True)
         backward = backward_rates(sq, cfg, q, k, v, stream)
 
+    kpass = None
+    if not args.no_tilings and cfg.name == "highres_bf16":
+        print("[bench] three-level operator", file=sys.stderr, flush=True)
+        kpass = kpass_rates(sq, q, k, v, H, stream)
+
     tilings = None
     if not args.no_tilings and cfg.name == "highres_bf16":
         print("[bench] other tilings of the workload", file=sys.stderr, flush=True)
@@ -252,6 +258,7 @@ def main():
         "permutations": perms,
         "tilings": tilings,
         "backward": backward,
+        "kpass": kpass,
     }
     print(json.dumps(line), flush=True)
 
@@ -311,6 +318,27 @@ def backward_rates(sq, cfg, q, k, v, stream):
     return {"forward_train_ms": round(ms_f, 4), "backward_ms": round(ms_b, 4),
             "backward_tflops": round(flops / ms_b / 1e9, 1),
             "backward_flops": flops, "train_step_ms": round(ms_f + ms_b, 4)}
+
+
+def kpass_rates(sq, q, k, v, heads, stream):
+    """The three-level operator over the high-resolution grid: nested tiles 4x4x4 |
+    16x16x16 | 64x48x80, units of 64, 64 and 60 tokens (about n^(1/3) each), on the
+    workload's inputs; beside the two-pass forward it does 188 / 992 of the work."""
+    import torch
+
+    grid, tiles = (64, 48, 80), [(4, 4, 4), (16, 16, 16)]
+    out = torch.empty_like(q)
+    ws = torch.empty(sq.squad_kpass_workspace_size(grid, tiles, heads, 1, q.shape[-1], q.dtype),
+                     dtype=torch.uint8, device=q.device)
+    fwd = lambda: sq.squad_kpass_forward(q, k, v, grid, tiles, heads, out=out, workspace=ws, stream=stream)
+    fwd()
+    torch.cuda.synchronize()
+    ms = time_launches(fwd, stream, 20)
+    n = grid[0] * grid[1] * grid[2]
+    flops = 4.0 * q.shape[-1] * (64 + 64 + 60) * n * heads
+    del out, ws
+    return {"grid": list(grid), "tiles": [list(t) for t in tiles], "levels": 3, "unit_rows": [64, 64, 60],
+            "ms": round(ms, 4), "tokens_per_s": round(n / (ms * 1e-3), 1), "tflops": round(flops / ms / 1e9, 1)}
 
 
 def present_pairs(grid, tile):

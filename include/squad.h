@@ -188,6 +188,32 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
 int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]);
 
 /*
+ * More than two passes.  The pages name composing more than two passes as future
+ * work, trading depth for efficiency (technical summary, "Beperkingen en
+ * Conclusie").  The reading taken here: `levels` = k passes over nested tiles
+ * t1 | t2 | ... | t(k-1) | grid (tiles holds (k-1) x 3 int32 {tt, th, tw}, each
+ * tile dividing the next and the last dividing the grid, per axis).  Each axis
+ * coordinate splits into k digits (digit j: the position among the t(j)-tiles
+ * inside the t(j+1)-tile, t0 = one cell, tk = the grid); pass j is the standard
+ * softmax attention among the tokens that differ only in digit j, with the same
+ * q and k, and its output is the value stream of pass j + 1:
+ *   o_0 = v,  o_(j+1) = Attn_j(q, k, o_j),  out = o_k.
+ * k = 2 is squad_attn_forward with tile = t1.  With unit sizes about n^(1/k)
+ * the work is O(k n^(1+1/k)).  Whole tilings only (SQUAD_ERR_SHAPE if the tiles
+ * do not nest); 2 <= levels <= 8 (else SQUAD_ERR_INVALID_ARG).
+ * q, k, v, out token order [batch, n, heads, head_dim]; `workspace` holds the
+ * intermediate outputs in token order (fp16 for bf16 calls, fp32 for fp32),
+ * squad_kpass_workspace_size bytes (0 for invalid arguments).  One kernel
+ * launch per pass; other statuses as for squad_attn_forward.
+ */
+size_t squad_kpass_workspace_size(const int32_t grid[3], const int32_t* tiles, int32_t levels,
+                                  int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype);
+int squad_kpass_forward(const void* q, const void* k, const void* v, const int32_t grid[3],
+                        const int32_t* tiles, int32_t levels, int32_t heads, void* out,
+                        int32_t batch, int32_t head_dim, int32_t dtype, float scale,
+                        void* workspace, size_t workspace_bytes, squad_stream_t stream);
+
+/*
  * Local pass alone (Attn_L): o1 = softmax attention inside each window.
  * q, k, v, o1 token order [batch, n, heads, head_dim].
  */
@@ -258,6 +284,16 @@ int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* 
  * On a cut tiling, absent rows of the two token maps read -1 (the test the
  * kernels use to skip them).
  */
+/*
+ * Host-only: the element offsets the six-digit map of pass `level` of a k-level
+ * operator gives, in the order [batch][heads][units][rows] (rows = the level's
+ * digits row-major over (t, h, w); units = the other digits).  offsets must
+ * hold batch*heads*n entries.  The middle passes of squad_kpass_forward use
+ * this map; its first and last passes use the two-pass maps.
+ */
+int squad_debug_kpass_offsets(const int32_t grid[3], const int32_t* tiles, int32_t levels, int32_t level,
+                              int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets);
+
 int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t tile[3],
                             int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets);
 

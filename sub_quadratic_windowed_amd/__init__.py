@@ -35,6 +35,9 @@ __all__ = [
     "squad_attn_forward_train",
     "squad_attn_backward",
     "SquadAttention",
+    "squad_kpass_workspace_size",
+    "squad_kpass_forward",
+    "squad_debug_kpass_offsets",
     "DTYPE_CODES",
 ]
 
@@ -209,6 +212,36 @@ class SquadAttention(torch.autograd.Function):
         return dq, dk, dv, None, None, None
 
 
+def _tiles(tiles):
+    flat = [int(x) for t in tiles for x in t]
+    if len(flat) != 3 * len(tiles) or not tiles:
+        raise ValueError("tiles must be a non-empty list of (tt, th, tw)")
+    return (ctypes.c_int32 * len(flat))(*flat), len(tiles) + 1
+
+
+def squad_kpass_workspace_size(grid, tiles, heads, batch, head_dim, dtype):
+    """Bytes of workspace squad_kpass_forward needs (0 for invalid arguments)."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    arr, levels = _tiles(tiles)
+    return int(_lib.lib().squad_kpass_workspace_size(_lib.int3(grid), arr, levels, int(heads), int(batch),
+                                                     int(head_dim), code))
+
+
+def squad_kpass_forward(q, k, v, grid, tiles, heads=None, out=None, scale=None, workspace=None, stream=None):
+    """The operator with len(tiles) + 1 composed passes over nested tiles
+    tiles[0] | tiles[1] | ... | grid (include/squad.h); len(tiles) == 1 is
+    squad_attn_forward with tile = tiles[0]."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _out_like(out, q)
+    arr, levels = _tiles(tiles)
+    workspace = _workspace(workspace, squad_kpass_workspace_size(grid, tiles, Hh, B, d, q.dtype), q.device)
+    st = _lib.lib().squad_kpass_forward(
+        _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), arr, levels, Hh, _ptr(out), B, d, DTYPE_CODES[q.dtype],
+        _scale(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "squad_kpass_forward")
+    return out
+
+
 def squad_attn_forward_local(q, k, v, grid, tile, heads=None, scale=None, workspace=None, stream=None):
     """First half of squad_attn_forward: the local pass into the workspace (returned)."""
     q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
@@ -324,6 +357,18 @@ def squad_dense_attn_forward(q, k, v, out=None, scale=None, stream=None):
     st = _lib.lib().squad_dense_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, n, Hh, d,
                                              DTYPE_CODES[q.dtype], _scale(scale), _stream(stream, q.device))
     _check(st, "squad_dense_attn_forward")
+    return out
+
+
+def squad_debug_kpass_offsets(grid, tiles, level, heads, batch, head_dim):
+    """Host-side element offsets of pass `level`'s six-digit map; numpy int64."""
+    import numpy as np
+
+    arr, levels = _tiles(tiles)
+    out = np.zeros(int(batch) * int(heads) * int(grid[0]) * int(grid[1]) * int(grid[2]), dtype=np.int64)
+    st = _lib.lib().squad_debug_kpass_offsets(_lib.int3(grid), arr, levels, int(level), int(heads), int(batch),
+                                              int(head_dim), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    _check(st, "squad_debug_kpass_offsets")
     return out
 
 

@@ -36,6 +36,9 @@ EXPORTS = [
     "squad_attn_train_workspace_size",
     "squad_attn_forward_train",
     "squad_attn_backward",
+    "squad_kpass_workspace_size",
+    "squad_kpass_forward",
+    "squad_debug_kpass_offsets",
 ]
 
 _lib = None
@@ -64,6 +67,12 @@ def _declare(lib):
     lib.squad_attn_forward_train.restype = ctypes.c_int
     lib.squad_attn_backward.argtypes = [P, P, P, P, P, I3, I3, I32, P, P, P, I32, I32, I32, F, P, SZ, P]
     lib.squad_attn_backward.restype = ctypes.c_int
+    lib.squad_kpass_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32, I32]
+    lib.squad_kpass_workspace_size.restype = SZ
+    lib.squad_kpass_forward.argtypes = [P, P, P, I3, I3, I32, I32, P, I32, I32, I32, F, P, SZ, P]
+    lib.squad_kpass_forward.restype = ctypes.c_int
+    lib.squad_debug_kpass_offsets.argtypes = [I3, I3, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_int64)]
+    lib.squad_debug_kpass_offsets.restype = ctypes.c_int
     lib.squad_plan_tile.argtypes = [I3, I3]
     lib.squad_plan_tile.restype = ctypes.c_int
     for name in ("squad_local_pass", "squad_global_pass"):

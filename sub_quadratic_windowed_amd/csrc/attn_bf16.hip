@@ -172,8 +172,8 @@ struct Stage {
 
 // CUT: the grid is not a whole number of tiles; absent rows (the far edges' cut
 // tiles) are neither keys nor stored queries (row tables only, TAB).
-template <int D, int NW, typename VT, typename OT, bool TAB, bool CUT = false>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(AttnArgs a) {
+template <int D, int NW, typename VT, typename OT, bool TAB, bool CUT = false, typename Args = AttnArgs>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(Args a) {
   static_assert(TAB || !CUT, "cut tilings use the row tables");
   typedef Cfg<D, NW> C;
   typedef typename Vec<VT>::x8 vx8;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   }
 
   // lane l (< 32) locates key l of a block; lanes 32-63 mirror lanes 0-31
-  auto key_offset = [&](const RowMap& m, uint32_t kb) -> int32_t {
+  auto key_offset = [&](const auto& m, uint32_t kb) -> int32_t {
     return m.row_off(min(kb * BN + l32, L - 1));
   };
   const bool v_like_k = a.v_like_k != 0;
@@ -534,29 +534,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   }
 }
 
-template <int D, int NW, typename VT, typename OT>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+template <int D, int NW, typename VT, typename OT, typename Args>
+hipError_t launch(const Args& a, hipStream_t stream) {
   const uint32_t groups = (a.units + 7) / 8;
   const uint64_t blocks = (uint64_t)groups * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (a.cut.on) {
-    // (the host allows cut tilings only where both passes use the row tables)
-    if (a.L > TABLE_ROWS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
-  } else if (a.L <= TABLE_ROWS)
-    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
+  if constexpr (std::is_same<Args, AttnArgs>::value) {
+    if (a.cut.on) {
+      // (the host allows cut tilings only where both passes use the row tables)
+      if (a.L > TABLE_ROWS) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.cut.on) {
+    return hipErrorInvalidValue;
+  }
+  if (a.L <= TABLE_ROWS)
+    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, false, Args>), dim3((uint32_t)blocks), dim3(64 * NW),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, false>), dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, false, false, Args>), dim3((uint32_t)blocks), dim3(64 * NW),
+                       0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, typename VT, typename OT>
-hipError_t launch_nw(const AttnArgs& a, int nw, hipStream_t stream) {
+template <int D, typename VT, typename OT, typename Args>
+hipError_t launch_nw(const Args& a, int nw, hipStream_t stream) {
   return nw == 4 ? launch<D, 4, VT, OT>(a, stream) : launch<D, 2, VT, OT>(a, stream);
 }
 
-template <typename VT, typename OT>
-hipError_t launch_types(const AttnArgs& a, int head_dim, int nw, hipStream_t stream) {
+template <typename VT, typename OT, typename Args>
+hipError_t launch_types(const Args& a, int head_dim, int nw, hipStream_t stream) {
   if (head_dim == 128) return launch_nw<128, VT, OT>(a, nw, stream);
   if (head_dim == 64) return launch_nw<64, VT, OT>(a, nw, stream);
   return hipErrorInvalidValue;
@@ -581,6 +590,13 @@ hipError_t launch_attn_bf16(AttnArgs a, int head_dim, VType vtype, hipStream_t s
     case VType::kF16ToBf16: return launch_types<_Float16, __bf16>(a, head_dim, nw, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_bf16_k(AttnArgsK a, int head_dim, hipStream_t stream) {
+  const uint32_t tiles = (a.L + 31) / 32;
+  const int nw = pick_waves(a.L);
+  a.nchunks = (tiles + nw - 1) / nw;
+  return launch_types<_Float16, _Float16>(a, head_dim, nw, stream);
 }
 
 }  // namespace squad

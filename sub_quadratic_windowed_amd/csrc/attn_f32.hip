@@ -17,8 +17,8 @@ constexpr int QPB = 64;  // queries per workgroup
 
 // CUT: the grid is not a whole number of tiles; absent rows are neither keys nor
 // stored queries.
-template <int D, bool CUT>
-__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+template <int D, bool CUT, typename Args = AttnArgs>
+__global__ __launch_bounds__(256) void attn_f32_kernel(Args a) {
   constexpr int DL = D / 4;        // dimensions per lane
   constexpr int CPR = D / 4;       // 16-byte chunks per row (4 floats each)
   constexpr int CH = KB * CPR;     // chunks per K (or V) block
@@ -135,20 +135,32 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+template <int D, typename Args>
+hipError_t launch(const Args& a, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
-  if (a.cut.on)
-    hipLaunchKernelGGL((attn_f32_kernel<D, true>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_f32_kernel<D, false>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+  if constexpr (std::is_same<Args, AttnArgs>::value) {
+    if (a.cut.on) {
+      hipLaunchKernelGGL((attn_f32_kernel<D, true>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.cut.on) {
+    return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL((attn_f32_kernel<D, false, Args>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(AttnArgs a, int head_dim, hipStream_t stream) {
+  a.nchunks = (a.L + QPB - 1) / QPB;
+  if (head_dim == 128) return launch<128>(a, stream);
+  if (head_dim == 64) return launch<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_f32_k(AttnArgsK a, int head_dim, hipStream_t stream) {
   a.nchunks = (a.L + QPB - 1) / QPB;
   if (head_dim == 128) return launch<128>(a, stream);
   if (head_dim == 64) return launch<64>(a, stream);

@@ -338,6 +338,55 @@ BwdArgs bwd_args(const Geo& g, bool local, int32_t heads, int32_t batch, int32_t
   return a;
 }
 
+// ---- k levels: nested tiles ext[1] | ext[2] | ... | ext[k - 1] | grid
+constexpr int KMAX = 8;
+struct KGeo {
+  int k;
+  int64_t ext[KMAX + 1][3];   // ext[0] = one cell, ext[k] = the grid
+  int64_t n;
+};
+
+int make_kgeo(const int32_t grid[3], const int32_t* tiles, int32_t levels, KGeo& kg) {
+  if (!grid || levels < 2 || levels > KMAX || !tiles) return SQUAD_ERR_INVALID_ARG;
+  kg.k = levels;
+  for (int a = 0; a < 3; ++a) {
+    kg.ext[0][a] = 1;
+    kg.ext[levels][a] = grid[a];
+    for (int j = 1; j < levels; ++j) kg.ext[j][a] = tiles[3 * (j - 1) + a];
+  }
+  for (int j = 0; j <= levels; ++j)
+    for (int a = 0; a < 3; ++a)
+      if (kg.ext[j][a] <= 0) return SQUAD_ERR_INVALID_ARG;
+  for (int j = 0; j < levels; ++j)
+    for (int a = 0; a < 3; ++a)
+      if (kg.ext[j + 1][a] % kg.ext[j][a]) return SQUAD_ERR_SHAPE;
+  kg.n = (int64_t)grid[0] * grid[1] * grid[2];
+  if (kg.n >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  return SQUAD_OK;
+}
+
+// Pass j of k levels: rows = the level-j digits, units = (position inside the
+// level-j tile, index of the level-(j+1) tile); token-order tensors.
+RowMapK kpass_map(const KGeo& kg, int j, int64_t heads, int64_t d) {
+  const int64_t H = kg.ext[kg.k][1], W = kg.ext[kg.k][2];
+  const int64_t ts = heads * d, Ws = W * ts, Hs = H * Ws;
+  const int64_t* lo = kg.ext[j];
+  const int64_t* hi = kg.ext[j + 1];
+  RowMapK m;
+  m.sB = kg.n * ts;
+  m.sH = d;
+  m.row = mix32((uint32_t)(hi[1] / lo[1]), (uint32_t)(hi[2] / lo[2]), lo[0] * Hs, lo[1] * Ws, lo[2] * ts);
+  m.unit = mix((uint32_t)lo[1], (uint32_t)lo[2], Hs, Ws, ts);
+  m.outer = mix((uint32_t)(H / hi[1]), (uint32_t)(W / hi[2]), hi[0] * Hs, hi[1] * Ws, hi[2] * ts);
+  m.split = FastDiv((uint32_t)(lo[0] * lo[1] * lo[2]));
+  return m;
+}
+
+int64_t kpass_rows(const KGeo& kg, int j) {
+  return (kg.ext[j + 1][0] / kg.ext[j][0]) * (kg.ext[j + 1][1] / kg.ext[j][1]) *
+         (kg.ext[j + 1][2] / kg.ext[j][2]);
+}
+
 int run_bwd(const BwdArgs& a, int32_t head_dim, int32_t dtype, BwdTypes t, hipStream_t s) {
   if (a.units == 0 || a.L == 0) return SQUAD_OK;
   for (int kind = 0; kind < 2; ++kind) {
@@ -708,6 +757,104 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   al.dv = dv; al.mdv = al.mqk;
   al.final_pass = 1;
   return run_bwd(al, head_dim, dtype, BwdTypes{false, true}, s);
+}
+
+// ---- more than two passes
+
+size_t squad_kpass_workspace_size(const int32_t grid[3], const int32_t* tiles, int32_t levels, int32_t heads,
+                                  int32_t batch, int32_t head_dim, int32_t dtype) {
+  KGeo kg;
+  if (make_kgeo(grid, tiles, levels, kg) || check_common(heads, batch, head_dim, dtype)) return 0;
+  const size_t one = (size_t)heads * batch * kg.n * head_dim * (dtype == SQUAD_DTYPE_BF16 ? 2 : 4);
+  return levels > 2 ? 2 * one : one;
+}
+
+int squad_kpass_forward(const void* q, const void* k, const void* v, const int32_t grid[3],
+                        const int32_t* tiles, int32_t levels, int32_t heads, void* out, int32_t batch,
+                        int32_t head_dim, int32_t dtype, float scale, void* workspace,
+                        size_t workspace_bytes, squad_stream_t stream) {
+  KGeo kg;
+  int st = make_kgeo(grid, tiles, levels, kg);
+  if (st) return st;
+  st = check_common(heads, batch, head_dim, dtype);
+  if (st) return st;
+  const uint64_t bh = (uint64_t)heads * (uint64_t)batch;
+  if ((uint64_t)kg.n * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  for (int j = 0; j < levels; ++j)
+    if (too_many_units(bh, (uint64_t)(kg.n / kpass_rows(kg, j)), bh * (uint64_t)kg.n)) return SQUAD_ERR_SHAPE;
+  const size_t bytes = (size_t)bh * kg.n * head_dim * elem_bytes(dtype);
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  const size_t one = (size_t)bh * kg.n * head_dim * (dtype == SQUAD_DTYPE_BF16 ? 2 : 4);
+  const size_t need = levels > 2 ? 2 * one : one;
+  if (!workspace || workspace_bytes < need) return SQUAD_ERR_WORKSPACE;
+  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i)
+    if (overlap(in[i], bytes, workspace, need)) return SQUAD_ERR_ALIAS;
+  if (overlap(out, bytes, workspace, need)) return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* buf[2] = {(char*)workspace, (char*)workspace + one};
+  const bool bf16 = dtype == SQUAD_DTYPE_BF16;
+  for (int j = 0; j < levels; ++j) {
+    const uint32_t L = (uint32_t)kpass_rows(kg, j);
+    const uint32_t U = (uint32_t)(kg.n / L);
+    const void* vin = j == 0 ? v : buf[(j - 1) & 1];
+    void* o = j == levels - 1 ? out : buf[j & 1];
+    if (j == 0 || j == levels - 1) {
+      // the first and last levels are the two-pass operator's local pass (tile =
+      // the level-1 tile) and global pass (tile = the level-(k-1) tile)
+      Geo g;
+      const int ti = j == 0 ? 1 : levels - 1;
+      const int32_t tile[3] = {(int32_t)kg.ext[ti][0], (int32_t)kg.ext[ti][1], (int32_t)kg.ext[ti][2]};
+      st = make_geo(grid, tile, g);
+      if (st) return st;
+      AttnArgs a = attn_args(q, k, vin, o, L, U, heads, batch, head_dim, scale);
+      a.mqk = token_map(g, heads, head_dim, j == 0);
+      a.mv = a.mqk;
+      a.mo = a.mqk;
+      const VType vt = j == 0 ? VType::kBf16ToF16 : VType::kF16ToBf16;
+      st = run_attn(a, head_dim, dtype, s, vt);
+    } else {
+      const AttnArgs base = attn_args(q, k, vin, o, L, U, heads, batch, head_dim, scale);
+      AttnArgsK a;
+      memset(&a, 0, sizeof(a));
+      a.q = base.q; a.k = base.k; a.v = base.v; a.o = base.o;
+      a.L = base.L; a.U = base.U; a.heads = base.heads; a.BH = base.BH;
+      a.fBH = base.fBH; a.fHeads = base.fHeads; a.units = base.units; a.c = base.c;
+      a.mqk = kpass_map(kg, j, heads, head_dim);
+      a.mv = a.mqk;
+      a.mo = a.mqk;
+      a.v_like_k = 1;
+      if (a.units == 0) continue;
+      const hipError_t e = bf16 ? launch_attn_bf16_k(a, head_dim, s) : launch_attn_f32_k(a, head_dim, s);
+      st = e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+    }
+    if (st) return st;
+  }
+  return SQUAD_OK;
+}
+
+int squad_debug_kpass_offsets(const int32_t grid[3], const int32_t* tiles, int32_t levels, int32_t level,
+                              int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets) {
+  KGeo kg;
+  int st = make_kgeo(grid, tiles, levels, kg);
+  if (st) return st;
+  if (level < 0 || level >= levels || !offsets || heads <= 0 || batch <= 0 || head_dim <= 0)
+    return SQUAD_ERR_INVALID_ARG;
+  const RowMapK m = kpass_map(kg, level, heads, head_dim);
+  const uint32_t L = (uint32_t)kpass_rows(kg, level);
+  const uint32_t U = (uint32_t)(kg.n / L);
+  size_t i = 0;
+  for (uint32_t b = 0; b < (uint32_t)batch; ++b)
+    for (uint32_t h = 0; h < (uint32_t)heads; ++h)
+      for (uint32_t s = 0; s < U; ++s) {
+        const int64_t base = m.base(b, h, s);
+        for (uint32_t r = 0; r < L; ++r) offsets[i++] = base + m.row_off(r);
+      }
+  return SQUAD_OK;
 }
 
 }  // extern "C"

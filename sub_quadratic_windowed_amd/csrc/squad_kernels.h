@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "squad_map.h"
 
 namespace squad {
@@ -25,12 +27,13 @@ struct Cut {
   uint32_t sr[3];    // per-axis scale of the row's digit
 };
 
-struct AttnArgs {
+template <typename Map>
+struct AttnArgsT {
   const void* q;
   const void* k;
   const void* v;
   void* o;
-  RowMap mqk, mv, mo;
+  Map mqk, mv, mo;
   uint32_t L;        // rows (queries = keys) per unit
   uint32_t U;        // units per (batch, head)
   uint32_t heads;    // heads per batch element
@@ -43,6 +46,8 @@ struct AttnArgs {
   Cut cut;           // absent rows (cut tilings only; on == 0 otherwise)
   float* lse;        // optional: row statistics lse[u * L + r] = log2 sum_j exp2(c <q_r, k_j>)
 };
+typedef AttnArgsT<RowMap> AttnArgs;
+typedef AttnArgsT<RowMapK> AttnArgsK;   // six-digit units (middle passes of k levels)
 
 // The digits of unit s under the token map, for Cut tests of its rows.
 struct UnitDigits {
@@ -71,6 +76,9 @@ enum class VType { kBf16ToBf16, kBf16ToF16, kF16ToBf16 };
 
 hipError_t launch_attn_bf16(AttnArgs a, int head_dim, VType vtype, hipStream_t stream);
 hipError_t launch_attn_f32(AttnArgs a, int head_dim, hipStream_t stream);
+// middle passes of a k-level operator: fp16 values in, fp16 out (bf16 calls)
+hipError_t launch_attn_bf16_k(AttnArgsK a, int head_dim, hipStream_t stream);
+hipError_t launch_attn_f32_k(AttnArgsK a, int head_dim, hipStream_t stream);
 
 // Backward of one pass (the gradients of the unit attentions above), in two
 // launches over the same units and rows:

@@ -131,4 +131,21 @@ struct RowMap {
   __host__ __device__ __forceinline__ int32_t row_off(uint32_t r) const { return row.at(r); }
 };
 
+// A map whose unit index has six digits: s = hi * split + lo, lo and hi each a
+// three-digit mix.  The middle passes of a k-level tiling need it: their units
+// are (position inside the level-j tile, index of the level-(j+1) tile).
+struct RowMapK {
+  int64_t sB, sH;
+  Mix unit;       // lo = s % split -> offset
+  Mix outer;      // hi = s / split -> offset
+  FastDiv split;
+  Mix32 row;
+
+  __host__ __device__ __forceinline__ int64_t base(uint32_t b, uint32_t h, uint32_t s) const {
+    const uint32_t hi = split.div(s);
+    return (int64_t)b * sB + (int64_t)h * sH + unit.at(s - hi * split.d) + outer.at(hi);
+  }
+  __host__ __device__ __forceinline__ int32_t row_off(uint32_t r) const { return row.at(r); }
+};
+
 }  // namespace squad

@@ -255,3 +255,54 @@ def test_cut_tilings_at_the_half_pass_entry_points():
                   ctypes.c_float(0), None) == UNSUP
     for fn in (lib.squad_tile_gather, lib.squad_tile_scatter, lib.squad_window_to_group):
         assert fn(p(A), p(B), _lib.int3((3, 5, 7)), t, 2, 1, 64, 1, None) == SHAPE
+
+
+# ---------------------------------------------------------------- k-level maps (host-only)
+
+KPASS_SHAPES = [((4, 8, 8), [(1, 2, 2), (2, 4, 4)]), ((4, 4, 8), [(1, 2, 2), (2, 2, 4), (2, 4, 8)]),
+                ((2, 8, 4), [(2, 2, 1), (2, 4, 2)]), ((64, 48, 80), [(4, 4, 4), (16, 16, 16)])]
+
+
+@pytest.mark.parametrize("grid,tiles", KPASS_SHAPES)
+def test_kpass_maps_are_the_level_partitions(grid, tiles):
+    """Every level's six-digit map sends (unit, row) to the token the oracle's level
+    index puts there (same row order; units may be numbered differently)."""
+    heads, batch, d = 2, 1, 64
+    n = int(np.prod(grid))
+    for level in range(len(tiles) + 1):
+        idx = oracle.kpass_level_index(grid, tiles, level)           # [U, L] tokens
+        U, L = idx.shape
+        got = sq.squad_debug_kpass_offsets(grid, tiles, level, heads, batch, d).reshape(batch, heads, U, L)
+        for h in range(heads):
+            tok = (got[0, h] - h * d) // (heads * d)
+            assert ((got[0, h] - h * d) % (heads * d) == 0).all()
+            # each unit is a unit of the oracle, rows in the same order
+            assert np.array_equal(np.sort(tok[:, 0]), np.sort(idx[:, 0]))
+            pos = {int(t): i for i, t in enumerate(idx[:, 0])}
+            assert np.array_equal(tok, idx[[pos[int(t)] for t in tok[:, 0]]])
+        if n > 10000:
+            break
+
+
+def test_kpass_argument_checks():
+    lib = _lib.lib()
+    p = ctypes.c_void_p
+    ws = lambda g, t: sq.squad_kpass_workspace_size(g, t, 2, 1, 64, 1)
+    assert ws((4, 8, 8), [(1, 2, 2), (2, 4, 4)]) == 2 * 256 * 2 * 64 * 2
+    assert ws((4, 8, 8), [(1, 4, 4)]) == 256 * 2 * 64 * 2
+    assert ws((4, 8, 8), [(1, 4, 4), (2, 2, 8)]) == 0                 # not nested
+    assert ws((4, 8, 8), [(1, 2, 2)] * 8) == 0                         # more than 8 levels
+    arr = (ctypes.c_int32 * 6)(1, 2, 2, 2, 4, 4)
+    g = _lib.int3((4, 8, 8))
+    call = lambda levels=3, d=64, out=O, w=WS, wb=1 << 30: lib.squad_kpass_forward(
+        p(A), p(B), p(C), g, arr, levels, 2, p(out), 1, d, 1, ctypes.c_float(0), p(w), wb, None)
+    assert call(levels=1) == INVALID
+    assert call(d=96) == UNSUP
+    assert call(out=A) == ALIAS
+    assert call(w=0) == WORKSPACE
+    assert call(wb=2 * 256 * 2 * 64 * 2 - 1) == WORKSPACE
+    bad = (ctypes.c_int32 * 6)(1, 4, 4, 2, 2, 8)
+    assert lib.squad_kpass_forward(p(A), p(B), p(C), g, bad, 3, 2, p(O), 1, 64, 1, ctypes.c_float(0), p(WS),
+                                   1 << 30, None) == SHAPE
+    if _device_count() == 0:
+        assert call() == HIP
