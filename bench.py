@@ -15,7 +15,9 @@ workload, and a dense full-attention comparator on the 5B-DiT-shaped workload.
 Under `tilings`, the same inputs under the planner's compact tile and on a grid
 cut by the tiling (one column narrower); under `backward`, the training path
 (forward keeping its statistics, then the gradients) on the same inputs; under
-`kpass`, the three-level operator on the same inputs.
+`kpass`, the three-level operator on the same inputs; under `block`, the
+attention block (projections, attention, output projection) at the 5B-DiT shape
+with SQuad and with dense attention.
 """
 
 import argparse
@@ -224,6 +226,10 @@ def main():
         torch.cuda.empty_cache()
         dense = dense_comparator(sq, inputs, dev)
 
+    block = None
+    if not args.no_dense:
+        block = block_rates(sq, inputs, dev)
+
     base = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
@@ -259,6 +265,7 @@ def main():
         "tilings": tilings,
         "backward": backward,
         "kpass": kpass,
+        "block": block,
     }
     print(json.dumps(line), flush=True)
 
@@ -381,6 +388,43 @@ def tiling_rates(sq, q, k, v, heads, stream):
                      "tokens_per_s": round(n / (ms * 1e-3), 1), "tflops": round(flops / ms / 1e9, 1)}
         del o, ws
     return out
+
+
+def block_rates(sq, inputs, dev):
+    """The attention block at the 5B-DiT shape (hidden 3072 = 24 heads x 128, grid
+    32x24x40, tile 2x8x10): x -> fused QKV projection -> attention -> output
+    projection, with SQuad-Attention and with dense attention (the comparator).
+    Synthetic weights, N(0, 1/hidden)."""
+    import torch
+
+    cfg = inputs.CONFIGS["dit5b_bf16"]
+    hidden = cfg.heads * cfg.head_dim
+    g = torch.Generator(device=dev).manual_seed(90)
+    x = torch.randn(1, cfg.n, hidden, generator=g, device=dev).to(torch.bfloat16)
+    wqkv = (torch.randn(3 * hidden, hidden, generator=g, device=dev) / hidden ** 0.5).to(torch.bfloat16)
+    wo = (torch.randn(hidden, hidden, generator=g, device=dev) / hidden ** 0.5).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    ws = torch.empty(sq.squad_block_workspace_size(cfg.grid, cfg.tile, cfg.heads, 1, cfg.head_dim, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev)
+    run = lambda dense: sq.squad_block_forward(x, wqkv, wo, cfg.grid, cfg.tile, cfg.heads, y=y, dense=dense,
+                                               workspace=ws, stream=s)
+    run(False)
+    run(True)
+    torch.cuda.synchronize()
+    ms_sq = time_launches(lambda: run(False), s, 20)
+    ms_dense = time_launches(lambda: run(True), s, 5)
+    gemm_flops = 2.0 * cfg.n * hidden * 4 * hidden
+    attn_sq = 4.0 * cfg.head_dim * (cfg.window + cfg.windows) * cfg.n * cfg.heads
+    attn_dense = 4.0 * cfg.head_dim * cfg.n * cfg.n * cfg.heads
+    del x, y, ws
+    return {"workload": f"{cfg.name} block: hidden {hidden}, grid {'x'.join(map(str, cfg.grid))}, "
+                        f"tile {'x'.join(map(str, cfg.tile))}",
+            "squad_block_ms": round(ms_sq, 4), "dense_block_ms": round(ms_dense, 4),
+            "latency_ratio": round(ms_dense / ms_sq, 2),
+            "projection_gflop": round(gemm_flops / 1e9, 1),
+            "squad_block_tflops": round((gemm_flops + attn_sq) / ms_sq / 1e9, 1),
+            "dense_block_tflops": round((gemm_flops + attn_dense) / ms_dense / 1e9, 1)}
 
 
 def dense_comparator(sq, inputs, dev):

@@ -188,6 +188,33 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
 int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]);
 
 /*
+ * The attention block around the operator.  The pages time the attention per
+ * block of a 5B video DiT (technical summary, "Experimentele Resultaten": about
+ * 47 ms dense against 4 ms with SQuad, per step per block; abstract: about 11x
+ * lower attention latency).  This runs the block's attention path with given
+ * weights (no bias, no normalisation; the pages describe neither):
+ *   qkv = x w_qkv^T   (x [batch, n, hidden], w_qkv [3 hidden, hidden], nn.Linear
+ *                      layout; q, k, v are qkv's column blocks, each [n, heads, d])
+ *   a   = SQuad-Attention(q, k, v) (dense = 1: full softmax attention instead,
+ *                      the comparator)
+ *   y   = a w_out^T   (w_out [hidden, hidden]; y [batch, n, hidden])
+ * hidden = heads * head_dim.  The projections are plain GEMMs on rocBLAS (fp32
+ * accumulation, outputs rounded to `dtype`); the attention kernels read q, k and v
+ * in place from the projection's output rows (row stride 3 hidden).  `workspace`
+ * holds qkv, the operator's workspace and a (squad_block_workspace_size bytes).
+ * Statuses as for squad_attn_forward, plus SQUAD_ERR_SHAPE when n * 3 * hidden
+ * reaches 2^31.  Unlike every other entry point, the first call on a device
+ * creates that device's rocBLAS handle, which allocates its own device memory
+ * once, kept until the process ends.
+ */
+size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads, int32_t batch,
+                                  int32_t head_dim, int32_t dtype);
+int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, const int32_t grid[3],
+                        const int32_t tile[3], int32_t heads, void* y, int32_t batch, int32_t head_dim,
+                        int32_t dtype, float scale, int32_t dense, void* workspace, size_t workspace_bytes,
+                        squad_stream_t stream);
+
+/*
  * More than two passes.  The pages name composing more than two passes as future
  * work, trading depth for efficiency (technical summary, "Beperkingen en
  * Conclusie").  The reading taken here: `levels` = k passes over nested tiles

@@ -85,6 +85,7 @@ __all__ = [
     "squad_forward_stats",
     "kpass_level_index",
     "squad_kpass_forward",
+    "squad_block_forward",
 ]
 
 
@@ -476,3 +477,24 @@ def squad_kpass_forward(q, k, v, grid, tiles, scale=None):
         o = np.empty_like(v)
         o[:, idx] = ou.transpose(0, 2, 3, 1, 4)
     return o
+
+
+# ---- the attention block around the operator (the pages time attention per block
+# of a 5B video DiT; technical summary, "Experimentele Resultaten") ----
+
+def squad_block_forward(x, w_qkv, w_out, grid, tile, heads, scale=None, dense=False):
+    """y = Attn(q, k, v) w_out^T with [q | k | v] = x w_qkv^T, in float64.
+
+    x [B, n, hidden]; w_qkv [3 hidden, hidden] and w_out [hidden, hidden] in the
+    nn.Linear layout (out_features, in_features); q, k, v are the three column
+    blocks of the projection, each split into `heads` heads of hidden / heads.
+    Attn is squad_forward (dense=True: dense_attention, the comparator).  No bias
+    and no normalisation: the pages describe neither.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, n, hidden = x.shape
+    d = hidden // int(heads)
+    qkv = np.matmul(x, np.asarray(w_qkv, np.float64).T)                  # [B, n, 3 hidden]
+    q, k, v = (qkv[..., i * hidden:(i + 1) * hidden].reshape(B, n, heads, d) for i in range(3))
+    a = dense_attention(q, k, v, scale) if dense else squad_forward(q, k, v, grid, tile, scale)
+    return np.matmul(a.reshape(B, n, hidden), np.asarray(w_out, np.float64).T)

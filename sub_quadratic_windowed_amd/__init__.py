@@ -38,6 +38,8 @@ __all__ = [
     "squad_kpass_workspace_size",
     "squad_kpass_forward",
     "squad_debug_kpass_offsets",
+    "squad_block_workspace_size",
+    "squad_block_forward",
     "DTYPE_CODES",
 ]
 
@@ -240,6 +242,46 @@ def squad_kpass_forward(q, k, v, grid, tiles, heads=None, out=None, scale=None, 
         _scale(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st, "squad_kpass_forward")
     return out
+
+
+def squad_block_workspace_size(grid, tile, heads, batch, head_dim, dtype):
+    """Bytes of workspace squad_block_forward needs (0 for invalid arguments)."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.lib().squad_block_workspace_size(_lib.int3(grid), _lib.int3(tile), int(heads), int(batch),
+                                                     int(head_dim), code))
+
+
+def squad_block_forward(x, w_qkv, w_out, grid, tile, heads, y=None, scale=None, dense=False, workspace=None,
+                        stream=None):
+    """The attention block: y = SQuad(x w_qkv^T split into q, k, v) w_out^T (dense=True:
+    full attention instead).  x [batch, n, hidden], w_qkv [3 hidden, hidden], w_out
+    [hidden, hidden]; returns y [batch, n, hidden]."""
+    x = _tensor(x, "x", 3)
+    B, n, hidden = x.shape
+    Hh = int(heads)
+    if hidden % Hh:
+        raise ValueError(f"hidden {hidden} is not a multiple of heads {Hh}")
+    d = hidden // Hh
+    w_qkv = _tensor(w_qkv, "w_qkv", 2, x.dtype, x.device)
+    w_out = _tensor(w_out, "w_out", 2, x.dtype, x.device)
+    if tuple(w_qkv.shape) != (3 * hidden, hidden) or tuple(w_out.shape) != (hidden, hidden):
+        raise ValueError("w_qkv must be [3 hidden, hidden] and w_out [hidden, hidden]")
+    T, H, W = (int(g) for g in grid)
+    if T * H * W != n:
+        raise ValueError(f"grid {tuple(grid)} has {T * H * W} tokens, x has {n}")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        y = _tensor(y, "y", 3, x.dtype, x.device)
+        if y.shape != x.shape:
+            raise ValueError(f"y shape {tuple(y.shape)} != {tuple(x.shape)}")
+    workspace = _workspace(workspace, squad_block_workspace_size(grid, tile, Hh, B, d, x.dtype), x.device)
+    st = _lib.lib().squad_block_forward(
+        _ptr(x), _ptr(w_qkv), _ptr(w_out), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(y), B, d,
+        DTYPE_CODES[x.dtype], _scale(scale), 1 if dense else 0, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, x.device))
+    _check(st, "squad_block_forward")
+    return y
 
 
 def squad_attn_forward_local(q, k, v, grid, tile, heads=None, scale=None, workspace=None, stream=None):

@@ -39,6 +39,8 @@ EXPORTS = [
     "squad_kpass_workspace_size",
     "squad_kpass_forward",
     "squad_debug_kpass_offsets",
+    "squad_block_workspace_size",
+    "squad_block_forward",
 ]
 
 _lib = None
@@ -73,6 +75,10 @@ def _declare(lib):
     lib.squad_kpass_forward.restype = ctypes.c_int
     lib.squad_debug_kpass_offsets.argtypes = [I3, I3, I32, I32, I32, I32, I32, ctypes.POINTER(ctypes.c_int64)]
     lib.squad_debug_kpass_offsets.restype = ctypes.c_int
+    lib.squad_block_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32]
+    lib.squad_block_workspace_size.restype = SZ
+    lib.squad_block_forward.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, I32, P, SZ, P]
+    lib.squad_block_forward.restype = ctypes.c_int
     lib.squad_plan_tile.argtypes = [I3, I3]
     lib.squad_plan_tile.restype = ctypes.c_int
     for name in ("squad_local_pass", "squad_global_pass"):

@@ -62,7 +62,8 @@ def build(verbose=False):
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
-    outs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
+    outs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
+                      "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]))
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:

@@ -5,7 +5,10 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
+
+#include <rocblas/rocblas.h>
 
 #include "squad.h"
 #include "squad_kernels.h"
@@ -78,9 +81,11 @@ Mix32 linear32(int64_t stride) { return mix32(1, 1, stride, 0, 0); }
 
 // Token order [B, n, heads, d]: the window part and the offset part of a token index.
 // (nh, nw, strides) of the window digits and (th, tw, strides) of the offset digits.
-RowMap token_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
+// ts: elements from one token's row to the next (heads * d for [B, n, heads, d];
+// larger when q, k and v are slices of one fused projection output)
+RowMap token_map(const Geo& g, int64_t heads, int64_t d, bool by_window, int64_t ts = 0) {
   RowMap m;
-  const int64_t ts = heads * d;
+  if (ts == 0) ts = heads * d;
   m.sB = g.n * ts;
   m.sH = d;
   const int64_t w2 = g.tt * g.H * g.W * ts, w1 = g.th * g.W * ts, w0 = g.tw * ts;
@@ -268,10 +273,10 @@ void set_cut(Args& a, const Geo& g, bool by_window) {
 // would take about half of the 1.5e-2 error budget; fp16 costs the same bytes).
 int forward_local(const void* q, const void* k, const void* v, const Geo& g, int32_t heads, int32_t batch,
                   int32_t head_dim, int32_t dtype, float scale, void* workspace, hipStream_t s,
-                  float* lse = nullptr) {
+                  float* lse = nullptr, int64_t in_ts = 0) {
   AttnArgs a = attn_args(q, k, v, workspace, (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, scale);
   a.lse = lse;
-  a.mqk = token_map(g, heads, head_dim, true);
+  a.mqk = token_map(g, heads, head_dim, true, in_ts);
   a.mv = a.mqk;
   a.mo = group_major_map(g, heads, head_dim, true);
   set_cut(a, g, true);
@@ -282,12 +287,12 @@ int forward_local(const void* q, const void* k, const void* v, const Geo& g, int
 // stream is the local output in the workspace; the output goes to token order.
 int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_t heads, int32_t batch,
                    int32_t head_dim, int32_t dtype, float scale, const void* workspace, hipStream_t s,
-                   float* lse = nullptr) {
+                   float* lse = nullptr, int64_t in_ts = 0) {
   AttnArgs a = attn_args(q, k, workspace, out, (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, scale);
   a.lse = lse;
-  a.mqk = token_map(g, heads, head_dim, false);
+  a.mqk = token_map(g, heads, head_dim, false, in_ts);
   a.mv = group_major_map(g, heads, head_dim, false);
-  a.mo = a.mqk;
+  a.mo = token_map(g, heads, head_dim, false);
   set_cut(a, g, false);
   return run_attn(a, head_dim, dtype, s, VType::kF16ToBf16);
 }
@@ -855,6 +860,134 @@ int squad_debug_kpass_offsets(const int32_t grid[3], const int32_t* tiles, int32
         for (uint32_t r = 0; r < L; ++r) offsets[i++] = base + m.row_off(r);
       }
   return SQUAD_OK;
+}
+
+}  // extern "C"
+
+// ---- the block around the operator: fused QKV projection, attention, output
+// projection (plain GEMMs on rocBLAS; the attention reads q, k, v straight out of
+// the projection's output rows)
+namespace {
+
+std::mutex g_blas_mu;
+rocblas_handle g_blas[64];
+
+// y[M, N] = x[M, K] w[N, K]^T, all row-major (rocBLAS is column-major: y^T = w x^T)
+int gemm_xwt(rocblas_handle hnd, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+             int32_t dtype) {
+  const float one = 1.f, zero = 0.f;
+  const rocblas_datatype t = dtype == SQUAD_DTYPE_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  const rocblas_status st = rocblas_gemm_ex(hnd, rocblas_operation_transpose, rocblas_operation_none,
+                                            (rocblas_int)N, (rocblas_int)M, (rocblas_int)K, &one, w, t,
+                                            (rocblas_int)K, x, t, (rocblas_int)K, &zero, y, t, (rocblas_int)N, y,
+                                            t, (rocblas_int)N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
+                                            0, 0);
+  return st == rocblas_status_success ? SQUAD_OK : SQUAD_ERR_HIP;
+}
+
+struct BlockLayout {
+  size_t qkv, ws, attn, total;
+};
+
+int block_layout(const Geo& g, int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype, BlockLayout& b) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t esz = elem_bytes(dtype);
+  const size_t rows = (size_t)batch * (size_t)g.n;
+  const size_t hidden = (size_t)heads * head_dim;
+  size_t bytes = 0, wbytes = 0;
+  Geo g2;
+  const int32_t grid[3] = {(int32_t)g.T, (int32_t)g.H, (int32_t)g.W};
+  const int32_t tile[3] = {(int32_t)g.tt, (int32_t)g.th, (int32_t)g.tw};
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g2, bytes, &wbytes, true);
+  if (st) return st;
+  b.qkv = 0;
+  b.ws = al(rows * 3 * hidden * esz);
+  b.attn = al(b.ws + wbytes);
+  b.total = al(b.attn + rows * hidden * esz);
+  return SQUAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads, int32_t batch,
+                                  int32_t head_dim, int32_t dtype) {
+  Geo g;
+  size_t bytes = 0;
+  if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true)) return 0;
+  BlockLayout b;
+  if (block_layout(g, heads, batch, head_dim, dtype, b)) return 0;
+  return b.total;
+}
+
+int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, const int32_t grid[3],
+                        const int32_t tile[3], int32_t heads, void* y, int32_t batch, int32_t head_dim,
+                        int32_t dtype, float scale, int32_t dense, void* workspace, size_t workspace_bytes,
+                        squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true);
+  if (st) return st;
+  if (dense != 0 && dense != 1) return SQUAD_ERR_INVALID_ARG;
+  BlockLayout lay;
+  st = block_layout(g, heads, batch, head_dim, dtype, lay);
+  if (st) return st;
+  const int64_t hidden = (int64_t)heads * head_dim;
+  // the attention addresses q, k, v rows (stride 3 * hidden) with 32-bit offsets
+  if (g.n * 3 * hidden >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  if ((int64_t)batch * g.n >= (int64_t(1) << 31) || 3 * hidden >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  const size_t wq_bytes = (size_t)3 * hidden * hidden * elem_bytes(dtype);
+  const size_t wo_bytes = (size_t)hidden * hidden * elem_bytes(dtype);
+  if (!x || !w_qkv || !w_out || !y) return SQUAD_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < lay.total) return SQUAD_ERR_WORKSPACE;
+  if (misaligned(x) || misaligned(w_qkv) || misaligned(w_out) || misaligned(y) || misaligned(workspace))
+    return SQUAD_ERR_ALIGN;
+  if (overlap(y, bytes, x, bytes) || overlap(y, bytes, w_qkv, wq_bytes) || overlap(y, bytes, w_out, wo_bytes) ||
+      overlap(y, bytes, workspace, lay.total) || overlap(x, bytes, workspace, lay.total) ||
+      overlap(w_qkv, wq_bytes, workspace, lay.total) || overlap(w_out, wo_bytes, workspace, lay.total))
+    return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SQUAD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_blas_mu);
+  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) return SQUAD_ERR_HIP;
+  rocblas_handle hnd = g_blas[dev];
+  hipStream_t s = (hipStream_t)stream;
+  if (rocblas_set_stream(hnd, s) != rocblas_status_success) return SQUAD_ERR_HIP;
+
+  char* ws = (char*)workspace;
+  const size_t esz = elem_bytes(dtype);
+  const int64_t M = (int64_t)batch * g.n;
+  char* qkv = ws + lay.qkv;
+  char* attn = ws + lay.attn;
+  st = gemm_xwt(hnd, x, w_qkv, qkv, M, 3 * hidden, hidden, dtype);
+  if (st) return st;
+  const char* q = qkv;
+  const char* k = qkv + hidden * esz;
+  const char* v = qkv + 2 * hidden * esz;
+  if (dense) {
+    // comparator: full softmax attention over all n tokens, same projections
+    AttnArgs a = attn_args(q, k, v, attn, (uint32_t)g.n, 1, heads, batch, head_dim, scale);
+    RowMap m;
+    m.sB = g.n * 3 * hidden;
+    m.sH = head_dim;
+    m.unit = linear(0);
+    m.row = linear32(3 * hidden);
+    a.mqk = m; a.mv = m;
+    a.mo = m;
+    a.mo.sB = g.n * hidden;
+    a.mo.row = linear32(hidden);
+    st = run_attn(a, head_dim, dtype, s);
+  } else {
+    st = forward_local(q, k, v, g, heads, batch, head_dim, dtype, scale, ws + lay.ws, s, nullptr, 3 * hidden);
+    if (!st)
+      st = forward_global(q, k, attn, g, heads, batch, head_dim, dtype, scale, ws + lay.ws, s, nullptr,
+                          3 * hidden);
+  }
+  if (st) return st;
+  return gemm_xwt(hnd, attn, w_out, y, M, hidden, hidden, dtype);
 }
 
 }  // extern "C"

@@ -153,3 +153,34 @@ def test_kpass_battery_rejects_mutant(name, monkeypatch):
     KMUTANTS[name](monkeypatch)
     with pytest.raises((AssertionError, ValueError)):
         kpass_battery()
+
+
+# ---------------------------------------------------------------- the attention block (oracle)
+
+def test_block_with_identity_projections_is_the_operator():
+    grid, tile, heads, d = (2, 4, 6), (2, 2, 3), 2, 4
+    hidden = heads * d
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 48, hidden))
+    eye = np.eye(hidden)
+    y = oracle.squad_block_forward(x, np.concatenate([eye, eye, eye]), eye, grid, tile, heads)
+    xh = x.reshape(1, 48, heads, d)
+    np.testing.assert_allclose(y, oracle.squad_forward(xh, xh, xh, grid, tile).reshape(1, 48, hidden), atol=1e-13)
+
+
+def test_block_projections_enter_as_plain_products():
+    """Zero query weights: every pass averages uniformly, so y is the mean over all
+    tokens of x w_v^T, through w_out (a closed form of the three products)."""
+    grid, tile, heads, d = (2, 4, 6), (2, 2, 3), 2, 4
+    hidden = heads * d
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 48, hidden))
+    wq = np.zeros((hidden, hidden))
+    wk, wv, wo = (rng.standard_normal((hidden, hidden)) for _ in range(3))
+    y = oracle.squad_block_forward(x, np.concatenate([wq, wk, wv]), wo, grid, tile, heads)
+    want = (x @ wv.T).mean(axis=1, keepdims=True) @ wo.T
+    np.testing.assert_allclose(y, np.broadcast_to(want, y.shape), atol=1e-12)
+    # dense comparator with a single window equals the operator (tile = grid)
+    w = np.concatenate([rng.standard_normal((hidden, hidden)) for _ in range(3)])
+    np.testing.assert_allclose(oracle.squad_block_forward(x, w, wo, grid, grid, heads),
+                               oracle.squad_block_forward(x, w, wo, grid, tile, heads, dense=True), atol=1e-12)
