@@ -57,6 +57,14 @@ struct BCfg {
   static_assert(VPW * NW == VINS && VPW >= 1, "loads split evenly over the waves");
 };
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -96,6 +104,15 @@ struct BStage {
   static __device__ __forceinline__ char* ptr() {
     __shared__ __attribute__((aligned(1024))) __bf16 buf[BN * D];
     return (char*)buf;
+  }
+};
+
+// One stage of a query block's row statistics: lse in slots 0..31, D in 32..63.
+template <int I>
+struct StatStage {
+  static __device__ __forceinline__ float* ptr() {
+    __shared__ __attribute__((aligned(16))) float buf[2 * BN];
+    return buf;
   }
 };
 
@@ -281,9 +298,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
   const float c = a.c;
 
-  auto step = [&](uint32_t kb, auto st_tag) {
+  // three stages: block kb sits in stage kb % 3 and is requested two steps ahead.
+  // ALL: block kb + 2 exists (known at compile time, so the main loop's steps
+  // have no conditional loads and the compiler's waits before the LDS reads stay
+  // per stage instead of draining every load)
+  auto step = [&](uint32_t kb, auto st_tag, auto all_tag) {
     constexpr int ST = decltype(st_tag)::value;
-    if (kb + 1 < nkb) issue(kb + 1, std::integral_constant<int, ST ^ 1>{});
+    constexpr bool ALL = decltype(all_tag)::value;
+    const bool has2 = ALL || kb + 2 < nkb;
+    if (has2) issue(kb + 2, std::integral_constant<int, (ST + 2) % 3>{});
     if (active) {
       const char* ks = BStage<D, ST, 0>::ptr();
       const char* vs = BStage<D, ST, 1>::ptr();
@@ -314,19 +337,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma(read_tr<D, false>(ks, lay, jk, mt), db[jk], acc[mt]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // this wave's loads of block kb + 1 have landed (those of kb + 2 may be in
+    // flight); the barrier publishes them and retires stage ST's readers
+    if (ALL) wait_vmcnt<2 * C::VPW>();
+    else if (has2) wait_vmcnt<2 * C::VPW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   };
 
   issue(0, std::integral_constant<int, 0>{});
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (nkb > 1) issue(1, std::integral_constant<int, 1>{});
+  // the prologue's row loads and block 0 have landed
+  if (nkb > 1) wait_vmcnt<2 * C::VPW>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
   uint32_t kb = 0;
-  for (; kb + 2 <= nkb; kb += 2) {
-    step(kb, std::integral_constant<int, 0>{});
-    step(kb + 1, std::integral_constant<int, 1>{});
+  for (; kb + 5 <= nkb; kb += 3) {
+    step(kb, std::integral_constant<int, 0>{}, std::true_type{});
+    step(kb + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    step(kb + 2, std::integral_constant<int, 2>{}, std::true_type{});
   }
-  if (kb < nkb) step(kb, std::integral_constant<int, 0>{});
+  for (; kb + 3 <= nkb; kb += 3) {
+    step(kb, std::integral_constant<int, 0>{}, std::false_type{});
+    step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    step(kb + 2, std::integral_constant<int, 2>{}, std::false_type{});
+  }
+  if (kb < nkb) step(kb, std::integral_constant<int, 0>{}, std::false_type{});
+  if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
 
   if (active && qok) {
     const int64_t base = a.mdq.base(p.b, p.h, p.s) + a.mdq.row_off(qi);
@@ -340,7 +377,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 template <int D, bool VF16, bool CUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(BwdArgs a) {
   typedef BCfg<D> C;
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BN], dsum_s[2][BN];
   UnitPos p;
   if (!unit_pos(a, p)) return;
   const uint32_t tid = threadIdx.x;
@@ -405,12 +441,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       __builtin_amdgcn_global_load_lds((const void*)(dg + 2 * a.mdo.row_off(r) + lay.ld_byte[i]),
                                        (lds_void_t*)(ds + ins * 1024), 16, 0, 0);
     }
-    // the block's row statistics (absent rows: lse = +inf, so their weights are 0)
-    if (wave == 0 && lane < BN) {
-      const uint32_t r = qb * BN + lane;
-      const bool ok = present(r);
-      lse_s[ST][lane] = ok ? a.lse[unit_rows + r] : INFINITY;
-      dsum_s[ST][lane] = ok ? a.dsum[unit_rows + r] : 0.f;
+    // the block's row statistics by one more direct load (lane i < 32: lse of row
+    // i, lane 32 + i: its D); every wave issues it, so the load counts and waits
+    // are the same in all waves (the duplicate writes carry the same values).
+    // Rows past the end or absent read a present row; the query mask drops them.
+    {
+      const uint32_t rr = load_row(qb * BN + l32);
+      const float* src = (half ? (const float*)a.dsum : a.lse) + unit_rows + rr;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)StatStage<ST>::ptr(), 4, 0, 0);
     }
   };
 
@@ -421,12 +459,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     for (int r = 0; r < 16; ++r) { dka[mt][r] = 0.f; dva[mt][r] = 0.f; }
   const float c = a.c;
 
-  auto step = [&](uint32_t qb, auto st_tag) {
+  // two stages: the next block is requested before the current one is used.
+  // ALL: the next block exists (known at compile time: no conditional loads in the
+  // main loop, so the compiler's waits before the LDS reads stay per stage)
+  auto step = [&](uint32_t qb, auto st_tag, auto all_tag) {
     constexpr int ST = decltype(st_tag)::value;
-    if (qb + 1 < nqb) issue(qb + 1, std::integral_constant<int, ST ^ 1>{});
+    constexpr bool ALL = decltype(all_tag)::value;
+    if (ALL || qb + 1 < nqb) issue(qb + 1, std::integral_constant<int, ST ^ 1>{});
     if (active) {
       const char* qs = BStage<D, ST, 2>::ptr();
       const char* ds = BStage<D, ST, 3>::ptr();
+      const float* stat = StatStage<ST>::ptr();
+      // present queries of the block: bit j for query qb * 32 + j, then this half's
+      uint32_t qm = 0xffffffffu;
+      if constexpr (CUT) {
+        qm = (uint32_t)__ballot(present(qb * BN + l32));
+      } else if ((qb + 1) * BN > L) {
+        qm = (1u << (L - qb * BN)) - 1u;   // fewer than 32 queries left
+      }
+      qm >>= 4 * half;
       f32x16 sc, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
@@ -440,14 +491,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // queries 8 g + 4 half + (0..3) of the block
-        const float4 ls = *(const float4*)&lse_s[ST][8 * g + 4 * half];
-        const float4 dd = *(const float4*)&dsum_s[ST][8 * g + 4 * half];
+        const float4 ls = *(const float4*)&stat[8 * g + 4 * half];
+        const float4 dd = *(const float4*)&stat[BN + 8 * g + 4 * half];
         const float lv[4] = {ls.x, ls.y, ls.z, ls.w};
         const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          const float pij = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e]));
+          const float pij = ((qm >> (8 * g + e)) & 1) ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e])) : 0.f;
           pb[r / 8][r % 8] = (__bf16)pij;
           sb[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dv4[e]));
         }
@@ -460,19 +511,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
           dka[mt] = mfma(read_tr<D, false>(qs, lay, jk, mt), sb[jk], dka[mt]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // the next block has landed; the barrier publishes it and retires stage ST
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   };
 
   issue(0, std::integral_constant<int, 0>{});
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);   // block 0 and the own V rows (LDS stores) are in place
+  __builtin_amdgcn_s_barrier();
   uint32_t qb = 0;
-  for (; qb + 2 <= nqb; qb += 2) {
-    step(qb, std::integral_constant<int, 0>{});
-    step(qb + 1, std::integral_constant<int, 1>{});
+  for (; qb + 3 <= nqb; qb += 2) {
+    step(qb, std::integral_constant<int, 0>{}, std::true_type{});
+    step(qb + 1, std::integral_constant<int, 1>{}, std::true_type{});
   }
-  if (qb < nqb) step(qb, std::integral_constant<int, 0>{});
+  if (qb < nqb) step(qb, std::integral_constant<int, 0>{}, std::false_type{});
+  if (qb + 1 < nqb) step(qb + 1, std::integral_constant<int, 1>{}, std::false_type{});
 
   if (active && kok) {
     const int64_t kbase = a.mdk.base(p.b, p.h, p.s) + a.mdk.row_off(kj);
