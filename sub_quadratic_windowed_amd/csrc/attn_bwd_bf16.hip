@@ -107,6 +107,17 @@ struct BStage {
   }
 };
 
+// Units of at most this many rows form their rows' byte offsets once per
+// workgroup, into an LDS table (two maps); longer units form them per load.
+constexpr int BT_ROWS = 512;
+template <bool TAB>
+struct RowTab {
+  static __device__ __forceinline__ int32_t* ptr() {
+    __shared__ int32_t t[TAB ? 2 * BT_ROWS : 1];
+    return t;
+  }
+};
+
 // One stage of a query block's row statistics: lse in slots 0..31, D in 32..63.
 template <int I>
 struct StatStage {
@@ -164,12 +175,10 @@ __device__ __forceinline__ bf16x8 read_tr(const char* stage, const Layout<D>& la
   const char* p = stage + 2 * (4 * jk * C::GRP + 128 * mt);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p + lay.tr_lo));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p + lay.tr_hi));
-  uint4 raw;
-  raw.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-  raw.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-  raw.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-  raw.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-  return frag<F16>(raw);
+  // the two halves side by side: a register pairing, no arithmetic
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return frag<F16>(__builtin_bit_cast(uint4, both));
 }
 
 struct UnitPos {
@@ -188,6 +197,10 @@ __device__ __forceinline__ bool unit_pos(const BwdArgs& a, UnitPos& p) {
   return true;
 }
 
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -221,7 +234,7 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
 
 // ---------------------------------------------------------------- kind A: dq (and D)
 
-template <int D, bool VF16, bool OF16, bool CUT>
+template <int D, bool VF16, bool OF16, bool CUT, bool TAB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(BwdArgs a) {
   typedef BCfg<D> C;
   UnitPos p;
@@ -269,6 +282,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
   }
   dsum = sum_halves(dsum);
+  // fp16 values (the global pass reads the local output): dP^T runs on fp16 MFMAs
+  // with the row's dout scaled by a power of two into fp16 range (max |dout| to
+  // [2^13, 2^14)), undone on the fp32 product, so V needs no conversion per block
+  typedef _Float16 f16x8l __attribute__((ext_vector_type(8)));
+  f16x8l dh[VF16 ? D / 16 : 1];
+  float dp_scale = 1.f;
+  if constexpr (VF16) {
+    float mx = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)df[kk][e]));
+    mx = max_halves(mx);
+    int ex = 0;
+    if (mx > 0.f) (void)frexpf(mx, &ex);   // mx = f 2^ex, f in [0.5, 1)
+    const float up = ldexpf(1.f, 14 - ex);
+    dp_scale = ldexpf(1.f, ex - 14);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dh[kk][e] = (_Float16)((float)df[kk][e] * up);
+  }
   const size_t row_id = (size_t)p.u * L + qi;
   const float lse = qok ? a.lse[row_id] : 0.f;
   if (qok && half == 0) a.dsum[row_id] = dsum;
@@ -276,6 +311,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   Layout<D> lay;
   lay.init(lane, wave);
   const uint32_t nkb = (L + BN - 1) / BN;
+  int32_t* tab = RowTab<TAB>::ptr();   // K rows, then V rows (byte offsets)
+  if constexpr (TAB) {
+    for (uint32_t r = tid; r < nkb * BN; r += 64 * NW) {
+      const uint32_t rr = load_row(r);
+      tab[r] = 2 * a.mqk.row_off(rr);
+      tab[BT_ROWS + r] = 2 * a.mv.row_off(rr);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the table is written
+    __builtin_amdgcn_s_barrier();
+  }
   auto issue = [&](uint32_t kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     char* ks = BStage<D, ST, 0>::ptr();
@@ -283,10 +328,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
-      const uint32_t r = load_row(kb * BN + lay.ld_row[i]);
-      __builtin_amdgcn_global_load_lds((const void*)(kg + 2 * a.mqk.row_off(r) + lay.ld_byte[i]),
+      int32_t ko, vo;
+      if constexpr (TAB) {
+        ko = tab[kb * BN + lay.ld_row[i]];
+        vo = tab[BT_ROWS + kb * BN + lay.ld_row[i]];
+      } else {
+        const uint32_t r = load_row(kb * BN + lay.ld_row[i]);
+        ko = 2 * a.mqk.row_off(r);
+        vo = 2 * a.mv.row_off(r);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(kg + (uint32_t)ko + lay.ld_byte[i]),
                                        (lds_void_t*)(ks + ins * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg + 2 * a.mv.row_off(r) + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(vg + (uint32_t)vo + lay.ld_byte[i]),
                                        (lds_void_t*)(vs + ins * 1024), 16, 0, 0);
     }
   };
@@ -316,7 +369,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         sc = mfma(read_rows<D, false>(ks, lay, kk), qf[kk], sc);
-        dp = mfma(read_rows<D, VF16>(vs, lay, kk), df[kk], dp);
+        if constexpr (VF16)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8l, *(const uint4*)(vs + lay.rd[kk & 1] + 256 * (kk >> 1))), dh[kk], dp, 0, 0, 0);
+        else
+          dp = mfma(read_rows<D, false>(vs, lay, kk), df[kk], dp);
       }
       // present keys of the block: bit j for key kb * 32 + j, then this half's bits
       uint32_t km = 0xffffffffu;
@@ -325,12 +382,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       } else if ((kb + 1) * BN > L) {
         km = (1u << (L - kb * BN)) - 1u;   // fewer than 32 keys left
       }
-      km >>= 4 * half;
       bf16x8 db[2];
+      if (km == 0xffffffffu) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pij = ((km >> (8 * (r / 4) + (r % 4))) & 1) ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse)) : 0.f;
-        db[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dsum));
+        for (int r = 0; r < 16; ++r)
+          db[r / 8][r % 8] = (__bf16)(__builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse)) * fmaf(dp[r], dp_scale, -dsum));
+      } else {
+        km >>= 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pij = __builtin_amdgcn_ubfe(km, 8 * (r / 4) + (r % 4), 1) ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lse)) : 0.f;
+          db[r / 8][r % 8] = (__bf16)(pij * fmaf(dp[r], dp_scale, -dsum));
+        }
       }
 #pragma unroll
       for (int jk = 0; jk < 2; ++jk)
@@ -374,7 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 // ---------------------------------------------------------------- kind B: dk, dv
 
-template <int D, bool VF16, bool CUT>
+template <int D, bool VF16, bool CUT, bool TAB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(BwdArgs a) {
   typedef BCfg<D> C;
   UnitPos p;
@@ -428,6 +491,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   lay.init(lane, wave);
   const size_t unit_rows = (size_t)p.u * L;
   const uint32_t nqb = (L + BN - 1) / BN;
+  int32_t* tab = RowTab<TAB>::ptr();   // Q rows, then dout rows (byte offsets)
+  if constexpr (TAB) {
+    for (uint32_t r = tid; r < nqb * BN; r += 64 * NW) {
+      const uint32_t rr = load_row(r);
+      tab[r] = 2 * a.mqk.row_off(rr);
+      tab[BT_ROWS + r] = 2 * a.mdo.row_off(rr);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the table is written
+    __builtin_amdgcn_s_barrier();
+  }
   auto issue = [&](uint32_t qb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     char* qs = BStage<D, ST, 2>::ptr();
@@ -435,10 +508,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
-      const uint32_t r = load_row(qb * BN + lay.ld_row[i]);
-      __builtin_amdgcn_global_load_lds((const void*)(qg + 2 * a.mqk.row_off(r) + lay.ld_byte[i]),
+      int32_t qo, dof;
+      if constexpr (TAB) {
+        qo = tab[qb * BN + lay.ld_row[i]];
+        dof = tab[BT_ROWS + qb * BN + lay.ld_row[i]];
+      } else {
+        const uint32_t r = load_row(qb * BN + lay.ld_row[i]);
+        qo = 2 * a.mqk.row_off(r);
+        dof = 2 * a.mdo.row_off(r);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(qg + (uint32_t)qo + lay.ld_byte[i]),
                                        (lds_void_t*)(qs + ins * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(dg + 2 * a.mdo.row_off(r) + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(dg + (uint32_t)dof + lay.ld_byte[i]),
                                        (lds_void_t*)(ds + ins * 1024), 16, 0, 0);
     }
     // the block's row statistics by one more direct load (lane i < 32: lse of row
@@ -477,6 +558,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       } else if ((qb + 1) * BN > L) {
         qm = (1u << (L - qb * BN)) - 1u;   // fewer than 32 queries left
       }
+      const bool all_q = qm == 0xffffffffu;
       qm >>= 4 * half;
       f32x16 sc, dp;
 #pragma unroll
@@ -488,6 +570,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                   *(const bf16x8*)(vrow_lds + (((uint32_t)(2 * kk) + half) ^ vxor) * 16), dp);
       }
       bf16x8 pb[2], sb[2];
+      if (!all_q) {
+        // queries past the end or absent: their scores become -inf (weight 0)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!__builtin_amdgcn_ubfe(qm, 8 * (r / 4) + (r % 4), 1)) sc[r] = -INFINITY;
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // queries 8 g + 4 half + (0..3) of the block
@@ -498,7 +586,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          const float pij = ((qm >> (8 * g + e)) & 1) ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e])) : 0.f;
+          const float pij = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e]));
           pb[r / 8][r % 8] = (__bf16)pij;
           sb[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dv4[e]));
         }
@@ -541,12 +629,16 @@ hipError_t launch(const BwdArgs& a, bool kind_b, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
+  // (the host allows cut tilings only where the units fit the row tables)
+  if (a.cut.on && a.L > BT_ROWS) return hipErrorInvalidValue;
   if (kind_b) {
-    if (a.cut.on) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false>), grid, block, 0, stream, a);
+    if (a.cut.on) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, true, true>), grid, block, 0, stream, a);
+    else if (a.L <= BT_ROWS) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, false>), grid, block, 0, stream, a);
   } else {
-    if (a.cut.on) hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false>), grid, block, 0, stream, a);
+    if (a.cut.on) hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, true, true>), grid, block, 0, stream, a);
+    else if (a.L <= BT_ROWS) hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
