@@ -86,6 +86,30 @@ def time_launches(fn, stream, iters):
     return start.elapsed_time(end) / iters
 
 
+def cold_and_copy(step, stream, dev, calls=20):
+    """Per-call forward times with the 256 MB last-level cache cleared first (a 1 GiB
+    scrub buffer written between calls, outside the timed region), median and min;
+    and the bandwidth of a plain 1 GiB device copy on the same card."""
+    import torch
+
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i in range(calls):
+        scrub.fill_(i & 0xff)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    dst = torch.empty_like(scrub)
+    dst.copy_(scrub)
+    torch.cuda.synchronize()
+    copy_ms = time_launches(lambda: dst.copy_(scrub), stream, 10)
+    del scrub, dst
+    return {"cold_median_ms": round(ms[len(ms) // 2], 4), "cold_min_ms": round(ms[0], 4), "calls": calls,
+            "copy_1gib_gbs": round(2.0 * (1 << 30) / copy_ms / 1e6, 1)}
+
+
 def cpu_baseline(cfg, qc, kc, vc, heads):
     """The float64 oracle as it stands, on `heads` of the workload's heads."""
     import numpy as np
@@ -201,6 +225,9 @@ def main():
         "source_digest": digest,
     }
 
+    print("[bench] cold-cache forward and copy bandwidth", file=sys.stderr, flush=True)
+    cold = cold_and_copy(step, stream, dev)
+
     perms = None
     if not args.no_permutations:
         perms = permutation_rates(sq, cfg, q, stream)
@@ -256,6 +283,10 @@ def main():
         },
         "tflops": round(tflops, 1),
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        # against min(MFMA peak, intensity x HBM peak), intensity = flops / (8 tensor passes)
+        "pct_roofline": round(100 * tflops / min(MFMA_BF16_PEAK_TFLOPS,
+                                                  flops / (2 * bytes_per_pass) * HBM_PEAK_GBS / 1e3), 2),
+        "cold": cold,
         "flops_per_step": flops,
         "kernels": kernels,
         "roofline": roofline,
@@ -427,12 +458,12 @@ def block_rates(sq, inputs, dev):
             "dense_block_tflops": round((gemm_flops + attn_dense) / ms_dense / 1e9, 1)}
 
 
-def dense_comparator(sq, inputs, dev):
-    """SQuad forward vs dense full attention on the 5B-DiT-shaped workload."""
+def dense_pair(sq, inputs, dev, name, dense_iters):
+    """SQuad forward vs dense full attention on one configuration's inputs."""
     import torch
 
-    cfg = inputs.CONFIGS["dit5b_bf16"]
-    print("[bench] dense comparator on dit5b_bf16", file=sys.stderr, flush=True)
+    cfg = inputs.CONFIGS[name]
+    print(f"[bench] dense comparator on {name}", file=sys.stderr, flush=True)
     qc, kc, vc = inputs.config_inputs(cfg)
     q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
     out = torch.empty_like(q)
@@ -445,10 +476,11 @@ def dense_comparator(sq, inputs, dev):
         f()
     torch.cuda.synchronize()
     ms_sq = time_launches(fwd, s, 20)
-    ms_dense = time_launches(dense, s, 5)
+    ms_dense = time_launches(dense, s, dense_iters)
     n, H, d, W, G = cfg.n, cfg.heads, cfg.head_dim, cfg.window, cfg.windows
     f_sq = 4.0 * d * (W + G) * n * H
     f_dense = 4.0 * d * n * n * H
+    del q, k, v, out, ws
     return {
         "workload": f"{cfg.name}: grid {'x'.join(map(str, cfg.grid))}, tile {'x'.join(map(str, cfg.tile))}, "
                     f"{H} heads, head_dim {d}",
@@ -459,6 +491,15 @@ def dense_comparator(sq, inputs, dev):
         "dense_tflops": round(f_dense / ms_dense / 1e9, 1),
         "squad_tflops": round(f_sq / ms_sq / 1e9, 1),
     }
+
+
+def dense_comparator(sq, inputs, dev):
+    """SQuad forward vs dense full attention: the 5B-DiT-shaped workload, plus the
+    small and the longer-clip configurations under `other_configs`."""
+    line = dense_pair(sq, inputs, dev, "dit5b_bf16", 5)
+    line["other_configs"] = [dense_pair(sq, inputs, dev, "small_bf16", 20),
+                             dense_pair(sq, inputs, dev, "long_bf16", 3)]
+    return line
 
 
 if __name__ == "__main__":
