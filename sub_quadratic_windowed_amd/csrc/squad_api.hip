@@ -918,6 +918,7 @@ size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], 
   if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true)) return 0;
   BlockLayout b;
   if (block_layout(g, heads, batch, head_dim, dtype, b)) return 0;
+  if (g.n * 3 * (int64_t)heads * head_dim >= (int64_t(1) << 31)) return 0;   // as squad_block_forward
   return b.total;
 }
 

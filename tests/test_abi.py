@@ -306,3 +306,61 @@ def test_kpass_argument_checks():
                                    1 << 30, None) == SHAPE
     if _device_count() == 0:
         assert call() == HIP
+
+
+# ---------------------------------------------------------------- training and block entry points (host-only)
+
+def test_training_entry_points_reject_bad_arguments():
+    lib = _lib.lib()
+    p = ctypes.c_void_p
+    g, t = _lib.int3((4, 8, 8)), _lib.int3((1, 4, 4))
+    need = sq.squad_attn_train_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 64, 1)
+    # O1 (fp16) + 3 per-row fp32 arrays + the local output's gradient + two fp32 accumulators
+    assert need >= 256 * 2 * 64 * 2 * 2 + 3 * 256 * 2 * 4 + 2 * 256 * 2 * 64 * 4
+    assert sq.squad_attn_train_workspace_size((4, 8, 8), (5, 4, 4), 2, 1, 64, 1) == 0
+    D, K, V, OUT, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+    def bwd(q=A, k=B, v=C, out=OUT, dout=DOUT, dq=D, dk=K, dv=V, ws=WS, wb=1 << 30, d=64, tile=t):
+        return lib.squad_attn_backward(p(q), p(k), p(v), p(out), p(dout), g, tile, 2, p(dq), p(dk), p(dv), 1, d, 1,
+                                       ctypes.c_float(0), p(ws), wb, None)
+    assert bwd(dout=0) == INVALID
+    assert bwd(dv=0) == INVALID
+    assert bwd(d=96) == UNSUP
+    assert bwd(tile=_lib.int3((5, 4, 4))) == SHAPE
+    assert bwd(dq=A) == ALIAS               # an output over an input
+    assert bwd(dk=D) == ALIAS               # two outputs overlapping
+    assert bwd(dv=WS) == ALIAS              # an output over the workspace
+    assert bwd(ws=0) == WORKSPACE
+    assert bwd(wb=need - 1) == WORKSPACE
+    assert bwd(dq=D + 4) == ALIGN
+    assert lib.squad_attn_forward_train(p(A), p(B), p(C), g, t, 2, p(O), 1, 64, 1, ctypes.c_float(0), p(WS),
+                                        need - 1, None) == WORKSPACE
+    if _device_count() == 0:
+        assert bwd() == HIP
+
+
+def test_block_entry_point_rejects_bad_arguments():
+    lib = _lib.lib()
+    p = ctypes.c_void_p
+    g, t = _lib.int3((4, 8, 8)), _lib.int3((1, 4, 4))
+    X, WQ, WO, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+    need = sq.squad_block_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 64, 1)
+    hidden = 128
+    assert need >= 256 * 3 * hidden * 2 + 256 * hidden * 2   # qkv and the attention output, bf16
+
+    def blk(x=X, wq=WQ, wo=WO, y=Y, dense=0, ws=WS, wb=1 << 30, d=64, grid=g, heads=2):
+        return lib.squad_block_forward(p(x), p(wq), p(wo), grid, t, heads, p(y), 1, d, 1, ctypes.c_float(0), dense,
+                                       p(ws), wb, None)
+    assert blk(x=0) == INVALID
+    assert blk(dense=2) == INVALID
+    assert blk(d=96) == UNSUP
+    assert blk(y=X) == ALIAS
+    assert blk(y=WQ + 64) == ALIAS
+    assert blk(ws=0) == WORKSPACE
+    assert blk(wb=need - 1) == WORKSPACE
+    assert blk(y=Y + 8) == ALIGN
+    # q, k, v rows at a stride of 3 hidden must keep 32-bit in-unit offsets:
+    # 245,760 tokens x 3 x 3072 passes 2^31
+    assert blk(grid=_lib.int3((64, 48, 80)), d=128, heads=24, wb=1 << 40) == SHAPE
+    assert sq.squad_block_workspace_size((64, 48, 80), (4, 12, 10), 24, 1, 128, 1) == 0
+    assert sq.squad_block_workspace_size((32, 24, 40), (2, 8, 10), 24, 1, 128, 1) > 0
