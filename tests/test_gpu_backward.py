@@ -81,6 +81,17 @@ def test_backward_matches_oracle(case):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_backward_with_a_given_scale(dtype):
+    grid, tile = (4, 6, 10), (2, 3, 5)
+    q, k, v, dout = rand_case((2, 240, 3, 64), dtype, 36, True)
+    out, ws = sq.squad_attn_forward_train(q, k, v, grid, tile, scale=0.3)
+    grads = sq.squad_attn_backward(q, k, v, out, dout, grid, tile, ws, scale=0.3)
+    torch.cuda.synchronize()
+    want = oracle.squad_backward(f64(q), f64(k), f64(v), f64(dout), grid, tile, scale=0.3)
+    check_grads(grads, want, dtype, "scale 0.3")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_forward_train_output_and_statistics(dtype):
     """forward_train's output is squad_attn_forward's, bit for bit; the row statistics
     it keeps are each pass's log-sum-exp (log2 domain), unit-major."""

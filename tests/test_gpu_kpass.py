@@ -46,6 +46,7 @@ KCASES = [
     ((16, 16, 16), [(4, 4, 4), (8, 8, 8)], 1, 1, 128, torch.bfloat16, False),     # units 64, 8, 8
     ((2, 24, 40), [(1, 8, 10), (2, 24, 40)], 1, 1, 128, torch.bfloat16, False),   # last level of size one
     ((4, 6, 10), [(1, 3, 5), (2, 6, 10)], 1, 2, 128, torch.float32, False),       # units 15, 8, 2
+    ((2, 32, 32), [(1, 1, 1), (2, 32, 32)], 1, 2, 128, torch.bfloat16, False),    # middle level of 2048 rows
 ]
 
 
