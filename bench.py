@@ -110,6 +110,23 @@ def cold_and_copy(step, stream, dev, calls=20):
             "copy_1gib_gbs": round(2.0 * (1 << 30) / copy_ms / 1e6, 1)}
 
 
+def mfma_probe(sq, stream, dev):
+    """The card's sustained bf16 MFMA rate with random operands (the library's
+    measuring kernel: nothing but independent 32x32x16 MFMA chains)."""
+    import torch
+
+    blocks, iters = 2048, 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    run = lambda: sq.squad_debug_mfma_probe(out, blocks, iters, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    ms = time_launches(run, stream, 5)
+    flops = blocks * 4.0 * iters * 4 * 32768.0
+    del out
+    return {"tflops": round(flops / ms / 1e9, 1), "frac_of_peak": round(flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel": "4 independent 32x32x16 bf16 MFMA chains per wave, hash-drawn operands, 8192 waves"}
+
+
 def cpu_baseline(cfg, qc, kc, vc, heads):
     """The float64 oracle as it stands, on `heads` of the workload's heads."""
     import numpy as np
@@ -227,6 +244,9 @@ def main():
 
     print("[bench] cold-cache forward and copy bandwidth", file=sys.stderr, flush=True)
     cold = cold_and_copy(step, stream, dev)
+    probe = mfma_probe(sq, stream, dev)
+    roofline["measured_mfma_tflops"] = probe["tflops"]
+    roofline["mfma_frac_of_measured"] = round(kernels[dom]["tflops"] / probe["tflops"], 4)
 
     perms = None
     if not args.no_permutations:
@@ -287,6 +307,7 @@ def main():
         "pct_roofline": round(100 * tflops / min(MFMA_BF16_PEAK_TFLOPS,
                                                   flops / (2 * bytes_per_pass) * HBM_PEAK_GBS / 1e3), 2),
         "cold": cold,
+        "mfma_probe": probe,
         "flops_per_step": flops,
         "kernels": kernels,
         "roofline": roofline,

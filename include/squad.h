@@ -321,6 +321,17 @@ int squad_dense_attn_forward(const void* q, const void* k, const void* v, void* 
 int squad_debug_kpass_offsets(const int32_t grid[3], const int32_t* tiles, int32_t levels, int32_t level,
                               int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets);
 
+/*
+ * Measuring kernel (not part of the operator): `blocks` workgroups of 256 threads,
+ * each wave running `iters` (rounded up to a multiple of 4) rounds of four
+ * independent 32x32x16 bf16 MFMAs on
+ * hash-drawn operands, 4 * 32768 flops per wave and round.  Timed by the caller,
+ * it gives the sustained MFMA rate of the card with random data, the ceiling
+ * against which the attention kernels' rate is read.  out holds blocks * 256
+ * floats (a checksum per lane).  SQUAD_ERR_INVALID_ARG for null out or sizes <= 0.
+ */
+int squad_debug_mfma_probe(float* out, int32_t blocks, int32_t iters, squad_stream_t stream);
+
 int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t tile[3],
                             int32_t heads, int32_t batch, int32_t head_dim, int64_t* offsets);
 

@@ -38,6 +38,7 @@ __all__ = [
     "squad_kpass_workspace_size",
     "squad_kpass_forward",
     "squad_debug_kpass_offsets",
+    "squad_debug_mfma_probe",
     "squad_block_workspace_size",
     "squad_block_forward",
     "DTYPE_CODES",
@@ -399,6 +400,17 @@ def squad_dense_attn_forward(q, k, v, out=None, scale=None, stream=None):
     st = _lib.lib().squad_dense_attn_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, n, Hh, d,
                                              DTYPE_CODES[q.dtype], _scale(scale), _stream(stream, q.device))
     _check(st, "squad_dense_attn_forward")
+    return out
+
+
+def squad_debug_mfma_probe(out, blocks, iters, stream=None):
+    """Run the measuring kernel (blocks x 256 threads, `iters` rounds of four bf16
+    MFMAs per wave) into `out` (float32, blocks * 256 entries on the GPU)."""
+    out = _tensor(out, "out", 1, torch.float32)
+    if out.numel() < int(blocks) * 256:
+        raise ValueError("out must hold blocks * 256 floats")
+    _check(_lib.lib().squad_debug_mfma_probe(_ptr(out), int(blocks), int(iters), _stream(stream, out.device)),
+           "squad_debug_mfma_probe")
     return out
 
 

@@ -41,6 +41,7 @@ EXPORTS = [
     "squad_debug_kpass_offsets",
     "squad_block_workspace_size",
     "squad_block_forward",
+    "squad_debug_mfma_probe",
 ]
 
 _lib = None
@@ -79,6 +80,8 @@ def _declare(lib):
     lib.squad_block_workspace_size.restype = SZ
     lib.squad_block_forward.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, I32, P, SZ, P]
     lib.squad_block_forward.restype = ctypes.c_int
+    lib.squad_debug_mfma_probe.argtypes = [P, I32, I32, P]
+    lib.squad_debug_mfma_probe.restype = ctypes.c_int
     lib.squad_plan_tile.argtypes = [I3, I3]
     lib.squad_plan_tile.restype = ctypes.c_int
     for name in ("squad_local_pass", "squad_global_pass"):

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsquad.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["squad_api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_bwd_bf16.hip", "attn_bwd_f32.hip", "permute.hip"]
+SOURCES = ["squad_api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_bwd_bf16.hip", "attn_bwd_f32.hip", "permute.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

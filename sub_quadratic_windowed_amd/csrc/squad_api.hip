@@ -991,4 +991,10 @@ int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, con
   return gemm_xwt(hnd, attn, w_out, y, M, hidden, hidden, dtype);
 }
 
+int squad_debug_mfma_probe(float* out, int32_t blocks, int32_t iters, squad_stream_t stream) {
+  if (!out || blocks <= 0 || iters <= 0) return SQUAD_ERR_INVALID_ARG;
+  if (misaligned(out)) return SQUAD_ERR_ALIGN;
+  return launch_mfma_probe(out, blocks, iters, (hipStream_t)stream) == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+}
+
 }  // extern "C"

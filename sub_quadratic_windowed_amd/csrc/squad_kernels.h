@@ -121,6 +121,10 @@ struct BwdTypes {
 };
 
 hipError_t launch_bwd_f32(BwdArgs a, int head_dim, bool kind_b, hipStream_t stream);
+
+// The measuring kernel: blocks x 256 threads, each wave `iters` rounds of four
+// independent 32x32x16 bf16 MFMAs; out[blocks * 256] receives a checksum per lane.
+hipError_t launch_mfma_probe(float* out, int32_t blocks, int32_t iters, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hipStream_t stream);
 
 // Row-permutation copy: rows e = (bh * U + s) * L + r for bh < BH, s < U, r < L;

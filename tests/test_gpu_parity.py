@@ -398,3 +398,13 @@ def test_cut_forward_on_the_planners_tile():
     out = sq.squad_attn_forward(q, k, v, grid, tile)
     torch.cuda.synchronize()
     assert maxerr(out, oracle.squad_forward(f64(q), f64(k), f64(v), grid, tile)) <= TOL[torch.bfloat16]
+
+
+def test_mfma_probe_runs_and_is_deterministic():
+    """The measuring kernel: finite per-lane checksums, identical across runs."""
+    out = torch.empty(8 * 256, dtype=torch.float32, device="cuda")
+    sq.squad_debug_mfma_probe(out, 8, 16)
+    a = out.clone()
+    sq.squad_debug_mfma_probe(out, 8, 16)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all() and torch.equal(a, out)
