@@ -14,22 +14,28 @@
 //                         registers: the S^T output layout is the B layout once
 //                         K^T is read with the matching key permutation)
 // so each lane owns one query and its statistics (lse, D) are per-lane scalars.
-// Kind B (one key chunk of 32 rows per wave): K^T and V^T in registers; per block
-// of 32 queries
+// Kind B (one key chunk of 32 rows per wave): K^T in registers, the workgroup's own
+// V rows in LDS (read as B operands; as registers they would leave no room for
+// the two accumulators); per block of 32 queries
 //   S  = Q * K^T,  dP = dout * V^T   (A = Q and dout rows from LDS)
 //   dv^T += dout^T * P,  dk^T += Q^T * dS   (A = transposing reads of dout and Q)
-// each lane owning one key; the block's 32 lse and D values sit in LDS.
+// each lane owning one key; the block's 32 lse and D values arrive in LDS by one
+// more direct load.
 //
 // LDS blocks hold 32 rows of 16-bit elements as 8 groups of 4 rows; in group g the
 // 16-byte chunk c of row r sits at slot 4 * (c ^ (g % 4)) + r % 4.  Row reads (A
 // operands, 16 bytes per lane) and transposing reads (ds_read_b64_tr_b16) are
 // then both free of bank conflicts, and a block is filled by direct global -> LDS
-// loads (one 16-byte chunk per lane).  Two stages: the next block is requested
-// before the current one is used.
+// loads (one 16-byte chunk per lane).  Kind A keeps three stages and requests each
+// block two steps ahead; kind B (whose own V rows take the room of a third stage)
+// keeps two and requests the next block before using the current one.  Units of
+// at most 512 rows form their rows' byte offsets once, into LDS tables.
 //
-// All products are bf16 with fp32 accumulation; fp16 operands (the local output,
-// the global pass's values) are converted to bf16 on the way to the MFMA.  dS and
-// P are rounded to bf16 for their products.
+// Products are bf16 with fp32 accumulation, except the global pass's dP^T: its
+// values are the fp16 local output, so it runs on fp16 MFMAs against dout scaled
+// per row by a power of two into fp16 range (undone on the fp32 result).  Elsewhere
+// fp16 operands are converted to bf16 on the way in.  dS and P are rounded to bf16
+// for their products.
 #include "squad_kernels.h"
 
 namespace squad {
