@@ -154,7 +154,9 @@ size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], i
  * layout and dtype).  `workspace` must hold what squad_attn_forward_train wrote
  * with the same q, k, v, grid, tile, heads, batch, head_dim, dtype and scale (its
  * scratch part is overwritten).  bf16 calls compute in fp32 with bf16 MFMA
- * operands (P and dS rounded to bf16) and round the gradients to bf16 once.
+ * operands (P and dS rounded to bf16; the global pass's <dout, o1> products on
+ * fp16 operands, dout scaled per row by a power of two) and round the gradients
+ * to bf16 once.
  * Statuses as for squad_attn_forward; the three outputs must not overlap each
  * other, an input or the workspace.  Work is enqueued on `stream`: four kernel
  * launches, no allocation, no synchronisation.
