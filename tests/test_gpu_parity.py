@@ -207,6 +207,38 @@ def test_large_config_sampled_groups(name):
     torch.cuda.empty_cache()
 
 
+def test_largest_row_offsets_sampled_groups():
+    """Rows addressed with 32-bit in-unit offsets close to their limit: 262,144 tokens
+    x 48 heads x 128 dims = 1.61e9 elements per tensor (the host rejects 2^31), and
+    G = 1024 offsets per group, past the global pass's LDS row tables.  The oracle
+    checks whole offset groups of the first and the last head (the largest
+    offsets) on a sample of offsets."""
+    grid, tile, Hh, d = (64, 64, 64), (4, 8, 8), 48, 128
+    n = 64 * 64 * 64
+    g = torch.Generator(device="cuda").manual_seed(61)
+    q, k, v = (torch.randn(1, n, Hh, d, generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    say("largest offsets: running the forward")
+    out = sq.squad_attn_forward(q, k, v, grid, tile, Hh)
+    torch.cuda.synchronize()
+    offsets = [0, 255]
+    for h in (0, Hh - 1):
+        say(f"  oracle on head {h}")
+        tokens, want = oracle.squad_forward_groups(f64(q[:, :, h:h + 1]), f64(k[:, :, h:h + 1]),
+                                                   f64(v[:, :, h:h + 1]), grid, tile, offsets)
+        got = out[:, torch.from_numpy(tokens.reshape(-1)).cuda(), h:h + 1]
+        got = got.reshape(1, len(offsets), -1, 1, d)
+        err = maxerr(got, want)
+        scale = float(np.max(np.abs(want)))
+        say(f"  head {h}: max-abs {err:.3e} over {want.size} outputs (max |out| {scale:.3f})")
+        assert err <= TOL[torch.bfloat16]
+        # outputs here average hundreds of values (max |out| ~ 0.2), so also hold the
+        # error to a few bf16 ulps of the output scale: a misplaced row would be off
+        # by the order of that scale
+        assert err <= 2e-2 * scale
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- properties at full size (no oracle)
 
 def test_highres_properties():
