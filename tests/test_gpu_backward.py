@@ -172,3 +172,25 @@ def test_backward_properties_at_highres_size():
     assert float(((sdv - sdo).abs() / scale).max()) < 4e-3
     sdk = dk.double().sum(dim=1)
     assert float((sdk.abs() / dk.double().abs().sum(dim=1)).max()) < 4e-3
+
+
+def test_training_on_a_side_stream():
+    """Forward_train and backward enqueued on a caller's own stream (not torch's
+    current one) give the same bits as on the current stream."""
+    grid, tile = (4, 6, 10), (2, 3, 5)
+    q, k, v, dout = rand_case((1, 240, 2, 128), torch.bfloat16, 37)
+    out, ws = sq.squad_attn_forward_train(q, k, v, grid, tile)
+    ref = sq.squad_attn_backward(q, k, v, out, dout, grid, tile, ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ws2 = torch.empty_like(ws)
+    out2 = torch.empty_like(out)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    sq.squad_attn_forward_train(q, k, v, grid, tile, out=out2, workspace=ws2, stream=side)
+    sq.squad_attn_backward(q, k, v, out2, dout, grid, tile, ws2, dq=grads[0], dk=grads[1], dv=grads[2],
+                           stream=side)
+    side.synchronize()
+    assert torch.equal(out, out2)
+    for a, b in zip(ref, grads):
+        assert torch.equal(a, b)
