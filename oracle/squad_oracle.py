@@ -54,7 +54,8 @@ More than two passes (squad_kpass_forward): the pages name composing more than
 two passes as future work.  The reading taken: nested tiles t1 | t2 | ... | grid
 split each axis coordinate into k digits; pass j attends among the tokens that
 differ only in digit j, and each pass's output is the next pass's value stream.
-k = 2 is the operator above.
+k = 2 is the operator above.  squad_kpass_backward is its chain rule over the
+levels.
 
 All arithmetic is float64.  Every function below is written from the definition,
 with numpy fancy indexing and numpy matmul as its only library steps.
@@ -85,6 +86,7 @@ __all__ = [
     "squad_forward_stats",
     "kpass_level_index",
     "squad_kpass_forward",
+    "squad_kpass_backward",
     "squad_block_forward",
 ]
 
@@ -477,6 +479,35 @@ def squad_kpass_forward(q, k, v, grid, tiles, scale=None):
         o = np.empty_like(v)
         o[:, idx] = ou.transpose(0, 2, 3, 1, 4)
     return o
+
+
+def squad_kpass_backward(q, k, v, dout, grid, tiles, scale=None):
+    """Gradients of squad_kpass_forward with respect to q, k and v, given dout.
+
+    The chain rule over the levels, from the last down: with o_0 = v and
+    o_(j+1) = Attn_j(q, k, o_j), the upstream gradient of o_k is dout, and level j's
+    backward at (q, k, o_j) given the gradient of o_(j+1) yields its parts of dq and
+    dk and the gradient of o_j; dq and dk are the sums over the levels, dv is the
+    gradient of o_0.  Two levels give squad_backward.
+    """
+    q, k, v, dout = (_as_bnhd(x, nm) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")))
+    s = _default_scale(q.shape[-1], scale)
+    levels = len(tiles) + 1
+    outs = [v]
+    for level in range(levels - 1):
+        idx = kpass_level_index(grid, tiles, level)
+        g = lambda x: x[:, idx].transpose(0, 3, 1, 2, 4)
+        ou = softmax_attention(g(q), g(k), g(outs[-1]), s)
+        o = np.empty_like(v)
+        o[:, idx] = ou.transpose(0, 2, 3, 1, 4)
+        outs.append(o)
+    dq, dk = np.zeros_like(q), np.zeros_like(k)
+    grad = np.asarray(dout, np.float64)
+    for level in reversed(range(levels)):
+        gq, gk, grad = _units_backward(q, k, outs[level], grad, kpass_level_index(grid, tiles, level), s)
+        dq += gq
+        dk += gk
+    return dq, dk, grad
 
 
 # ---- the attention block around the operator (the pages time attention per block

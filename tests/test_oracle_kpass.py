@@ -184,3 +184,61 @@ def test_block_projections_enter_as_plain_products():
     w = np.concatenate([rng.standard_normal((hidden, hidden)) for _ in range(3)])
     np.testing.assert_allclose(oracle.squad_block_forward(x, w, wo, grid, grid, heads),
                                oracle.squad_block_forward(x, w, wo, grid, tile, heads, dense=True), atol=1e-12)
+
+
+# ---------------------------------------------------------------- k-pass gradients (oracle)
+
+def torch_kpass(q, k, v, grid, tiles, scale):
+    """The k-pass operator as dense masked attentions in torch (one mask per level)."""
+    import torch
+    dig = level_digits(grid, tiles)
+    n = q.shape[1]
+    o = v
+    for j in range(len(dig)):
+        mask = np.ones((n, n), bool)
+        for l, dl in enumerate(dig):
+            if l != j:
+                mask &= (dl[:, None, :] == dl[None, :, :]).all(-1)
+        m = torch.from_numpy(mask)
+        lg = (scale * torch.einsum("bihd,bjhd->bhij", q, k)).masked_fill(~m, float("-inf"))
+        o = torch.einsum("bhij,bjhd->bihd", torch.softmax(lg, -1), o)
+    return o
+
+
+@pytest.mark.parametrize("grid,tiles", KCASES)
+def test_kpass_backward_matches_torch_autograd(grid, tiles):
+    import torch
+    q, k, v = rand_qkv(grid, 2, 2, 8, 11)
+    dout = np.random.default_rng(12).standard_normal(q.shape)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    torch_kpass(tq, tk, tv, grid, tiles, 0.45).backward(torch.from_numpy(dout))
+    got = oracle.squad_kpass_backward(q, k, v, dout, grid, tiles, 0.45)
+    for g, w in zip(got, (tq.grad, tk.grad, tv.grad)):
+        np.testing.assert_allclose(g, w.numpy(), atol=1e-12)
+
+
+def test_kpass_backward_two_levels_is_the_two_pass_backward():
+    grid, tile = (4, 8, 8), (1, 4, 4)
+    q, k, v = rand_qkv(grid, 1, 2, 8, 13)
+    dout = np.random.default_rng(14).standard_normal(q.shape)
+    for a, b in zip(oracle.squad_kpass_backward(q, k, v, dout, grid, [tile]),
+                    oracle.squad_backward(q, k, v, dout, grid, tile)):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def test_kpass_backward_central_differences():
+    grid, tiles = (2, 4, 4), [(1, 2, 2), (2, 2, 4)]
+    q, k, v = rand_qkv(grid, 1, 1, 4, 15)
+    dout = np.random.default_rng(16).standard_normal(q.shape)
+    grads = oracle.squad_kpass_backward(q, k, v, dout, grid, tiles)
+    rng = np.random.default_rng(17)
+    eps = 1e-6
+    for which in range(3):
+        u = rng.standard_normal(q.shape)
+        p_ = [q, k, v]
+        m_ = [q, k, v]
+        p_[which] = p_[which] + eps * u
+        m_[which] = m_[which] - eps * u
+        fd = (np.sum(dout * oracle.squad_kpass_forward(*p_, grid, tiles))
+              - np.sum(dout * oracle.squad_kpass_forward(*m_, grid, tiles))) / (2 * eps)
+        assert abs(fd - np.sum(grads[which] * u)) <= 1e-7 * max(1.0, abs(fd))
