@@ -243,6 +243,30 @@ int squad_kpass_forward(const void* q, const void* k, const void* v, const int32
                         void* workspace, size_t workspace_bytes, squad_stream_t stream);
 
 /*
+ * Training the k-level operator: the chain rule over the levels, from the last
+ * down (level j's backward at (q, k, o_j) given the gradient of o_(j+1) yields
+ * its parts of dq and dk and the gradient of o_j; dv is the gradient of o_0).
+ * squad_kpass_train_workspace_size: bytes of the workspace both calls share (the
+ * intermediate outputs, each level's row statistics, and the backward's scratch).
+ * squad_kpass_forward_train: squad_kpass_forward keeping that state.
+ * squad_kpass_backward: dq, dk, dv ([batch, n, heads, head_dim], the call's dtype)
+ * from q, k, v, the training forward's out and dout, with its workspace (same
+ * grid, tiles, heads, batch, head_dim, dtype and scale).  Precision and statuses
+ * as for squad_attn_backward; two kernel launches per level.
+ */
+size_t squad_kpass_train_workspace_size(const int32_t grid[3], const int32_t* tiles, int32_t levels,
+                                        int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype);
+int squad_kpass_forward_train(const void* q, const void* k, const void* v, const int32_t grid[3],
+                              const int32_t* tiles, int32_t levels, int32_t heads, void* out,
+                              int32_t batch, int32_t head_dim, int32_t dtype, float scale,
+                              void* workspace, size_t workspace_bytes, squad_stream_t stream);
+int squad_kpass_backward(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const int32_t grid[3], const int32_t* tiles, int32_t levels,
+                         int32_t heads, void* dq, void* dk, void* dv, int32_t batch, int32_t head_dim,
+                         int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                         squad_stream_t stream);
+
+/*
  * Local pass alone (Attn_L): o1 = softmax attention inside each window.
  * q, k, v, o1 token order [batch, n, heads, head_dim].
  */

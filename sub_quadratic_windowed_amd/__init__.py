@@ -39,6 +39,9 @@ __all__ = [
     "squad_kpass_forward",
     "squad_debug_kpass_offsets",
     "squad_debug_mfma_probe",
+    "squad_kpass_train_workspace_size",
+    "squad_kpass_forward_train",
+    "squad_kpass_backward",
     "squad_block_workspace_size",
     "squad_block_forward",
     "DTYPE_CODES",
@@ -283,6 +286,48 @@ def squad_block_forward(x, w_qkv, w_out, grid, tile, heads, y=None, scale=None, 
         workspace.numel() * workspace.element_size(), _stream(stream, x.device))
     _check(st, "squad_block_forward")
     return y
+
+
+def squad_kpass_train_workspace_size(grid, tiles, heads, batch, head_dim, dtype):
+    """Bytes of the workspace squad_kpass_forward_train and squad_kpass_backward share."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    arr, levels = _tiles(tiles)
+    return int(_lib.lib().squad_kpass_train_workspace_size(_lib.int3(grid), arr, levels, int(heads), int(batch),
+                                                           int(head_dim), code))
+
+
+def squad_kpass_forward_train(q, k, v, grid, tiles, heads=None, out=None, scale=None, workspace=None,
+                              stream=None):
+    """squad_kpass_forward keeping what squad_kpass_backward needs.  Returns (out, workspace)."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _out_like(out, q)
+    arr, levels = _tiles(tiles)
+    workspace = _workspace(workspace, squad_kpass_train_workspace_size(grid, tiles, Hh, B, d, q.dtype), q.device)
+    st = _lib.lib().squad_kpass_forward_train(
+        _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), arr, levels, Hh, _ptr(out), B, d, DTYPE_CODES[q.dtype],
+        _scale(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "squad_kpass_forward_train")
+    return out, workspace
+
+
+def squad_kpass_backward(q, k, v, out, dout, grid, tiles, workspace, heads=None, dq=None, dk=None, dv=None,
+                         scale=None, stream=None):
+    """Gradients (dq, dk, dv) of squad_kpass_forward given dout; `workspace` as left by
+    squad_kpass_forward_train on the same inputs."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _tensor(out, "out", 4, q.dtype, q.device)
+    dout = _tensor(dout, "dout", 4, q.dtype, q.device)
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have q's shape")
+    dq, dk, dv = (_out_like(x, q, nm) for x, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    arr, levels = _tiles(tiles)
+    workspace = _workspace(workspace, 0, q.device)
+    st = _lib.lib().squad_kpass_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _lib.int3(grid), arr, levels, Hh, _ptr(dq), _ptr(dk),
+        _ptr(dv), B, d, DTYPE_CODES[q.dtype], _scale(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st, "squad_kpass_backward")
+    return dq, dk, dv
 
 
 def squad_attn_forward_local(q, k, v, grid, tile, heads=None, scale=None, workspace=None, stream=None):

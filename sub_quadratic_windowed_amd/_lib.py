@@ -42,6 +42,9 @@ EXPORTS = [
     "squad_block_workspace_size",
     "squad_block_forward",
     "squad_debug_mfma_probe",
+    "squad_kpass_train_workspace_size",
+    "squad_kpass_forward_train",
+    "squad_kpass_backward",
 ]
 
 _lib = None
@@ -82,6 +85,12 @@ def _declare(lib):
     lib.squad_block_forward.restype = ctypes.c_int
     lib.squad_debug_mfma_probe.argtypes = [P, I32, I32, P]
     lib.squad_debug_mfma_probe.restype = ctypes.c_int
+    lib.squad_kpass_train_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32, I32]
+    lib.squad_kpass_train_workspace_size.restype = SZ
+    lib.squad_kpass_forward_train.argtypes = [P, P, P, I3, I3, I32, I32, P, I32, I32, I32, F, P, SZ, P]
+    lib.squad_kpass_forward_train.restype = ctypes.c_int
+    lib.squad_kpass_backward.argtypes = [P, P, P, P, P, I3, I3, I32, I32, P, P, P, I32, I32, I32, F, P, SZ, P]
+    lib.squad_kpass_backward.restype = ctypes.c_int
     lib.squad_plan_tile.argtypes = [I3, I3]
     lib.squad_plan_tile.restype = ctypes.c_int
     for name in ("squad_local_pass", "squad_global_pass"):

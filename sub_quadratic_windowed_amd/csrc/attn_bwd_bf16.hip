@@ -190,7 +190,8 @@ __device__ __forceinline__ bf16x8 read_tr(const char* stage, const Layout<D>& la
 struct UnitPos {
   uint32_t u, s, b, h, chunk;
 };
-__device__ __forceinline__ bool unit_pos(const BwdArgs& a, UnitPos& p) {
+template <typename Args>
+__device__ __forceinline__ bool unit_pos(const Args& a, UnitPos& p) {
   const uint32_t wg = blockIdx.x;
   const uint32_t jj = wg >> 3;
   p.chunk = jj % a.nchunks;
@@ -216,7 +217,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // r % 4) of this lane's row) as fp32 (accumulate or plain) or bf16.
 template <int D>
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float scale, uint32_t half,
-                                           bool final_pass, float* accp, __bf16* outp) {
+                                           uint32_t mode, float* accp, __bf16* outp) {
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
@@ -224,11 +225,11 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
       const int d0 = 32 * mt + 8 * g + 4 * half;
       float4 x = make_float4(acc[mt][4 * g] * scale, acc[mt][4 * g + 1] * scale, acc[mt][4 * g + 2] * scale,
                              acc[mt][4 * g + 3] * scale);
-      if (final_pass) {
-        if (accp) {
-          const float4 y = *(const float4*)(accp + d0);
-          x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
-        }
+      if (mode != kAccWrite && accp) {
+        const float4 y = *(const float4*)(accp + d0);
+        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      }
+      if (mode == kAccFinal) {
         bf16x4 w;
         w[0] = (__bf16)x.x; w[1] = (__bf16)x.y; w[2] = (__bf16)x.z; w[3] = (__bf16)x.w;
         *(bf16x4*)(outp + d0) = w;
@@ -240,8 +241,8 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
 
 // ---------------------------------------------------------------- kind A: dq (and D)
 
-template <int D, bool VF16, bool OF16, bool CUT, bool TAB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(BwdArgs a) {
+template <int D, bool VF16, bool OF16, bool CUT, bool TAB, typename Args = BwdArgs>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(Args a) {
   typedef BCfg<D> C;
   UnitPos p;
   if (!unit_pos(a, p)) return;
@@ -436,15 +437,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   if (active && qok) {
     const int64_t base = a.mdq.base(p.b, p.h, p.s) + a.mdq.row_off(qi);
-    store_rows<D>(acc, a.scale, half, a.final_pass != 0, a.dq_acc + base,
-                  a.final_pass ? (__bf16*)a.dq + base : nullptr);
+    store_rows<D>(acc, a.scale, half, a.final_pass, a.dq_acc + base,
+                  a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr);
   }
 }
 
 // ---------------------------------------------------------------- kind B: dk, dv
 
-template <int D, bool VF16, bool CUT, bool TAB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(BwdArgs a) {
+template <int D, bool VF16, bool CUT, bool TAB, typename Args = BwdArgs>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(Args a) {
   typedef BCfg<D> C;
   UnitPos p;
   if (!unit_pos(a, p)) return;
@@ -623,28 +624,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   if (active && kok) {
     const int64_t kbase = a.mdk.base(p.b, p.h, p.s) + a.mdk.row_off(kj);
-    store_rows<D>(dka, a.scale, half, a.final_pass != 0, a.dk_acc + kbase,
-                  a.final_pass ? (__bf16*)a.dk + kbase : nullptr);
+    store_rows<D>(dka, a.scale, half, a.final_pass, a.dk_acc + kbase,
+                  a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr);
     const int64_t vbase = a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(kj);
-    store_rows<D>(dva, 1.f, half, true, nullptr, (__bf16*)a.dv + vbase);
+    store_rows<D>(dva, 1.f, half, kAccFinal, nullptr, (__bf16*)a.dv + vbase);
   }
 }
 
-template <int D, bool VF16, bool OF16>
-hipError_t launch(const BwdArgs& a, bool kind_b, hipStream_t stream) {
+template <int D, bool VF16, bool OF16, typename Args>
+hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
-  // (the host allows cut tilings only where the units fit the row tables)
-  if (a.cut.on && a.L > BT_ROWS) return hipErrorInvalidValue;
+  if constexpr (std::is_same<Args, BwdArgs>::value) {
+    // (the host allows cut tilings only where the units fit the row tables)
+    if (a.cut.on) {
+      if (a.L > BT_ROWS) return hipErrorInvalidValue;
+      if (kind_b) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, true, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.cut.on) {
+    return hipErrorInvalidValue;
+  }
   if (kind_b) {
-    if (a.cut.on) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, true, true>), grid, block, 0, stream, a);
-    else if (a.L <= BT_ROWS) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, false>), grid, block, 0, stream, a);
+    if (a.L <= BT_ROWS) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, true, Args>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, false, Args>), grid, block, 0, stream, a);
   } else {
-    if (a.cut.on) hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, true, true>), grid, block, 0, stream, a);
-    else if (a.L <= BT_ROWS) hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, false>), grid, block, 0, stream, a);
+    if (a.L <= BT_ROWS)
+      hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, true, Args>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, false, Args>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -662,6 +672,13 @@ hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hip
   a.nchunks = (a.L + BM - 1) / BM;
   if (head_dim == 128) return launch_types<128>(a, t, kind_b, stream);
   if (head_dim == 64) return launch_types<64>(a, t, kind_b, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bf16_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream) {
+  a.nchunks = (a.L + BM - 1) / BM;
+  if (head_dim == 128) return launch<128, true, true>(a, kind_b, stream);
+  if (head_dim == 64) return launch<64, true, true>(a, kind_b, stream);
   return hipErrorInvalidValue;
 }
 

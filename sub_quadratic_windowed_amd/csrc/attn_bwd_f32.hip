@@ -34,7 +34,8 @@ struct F32Cfg {
 struct UnitPos {
   uint32_t u, s, b, h, chunk;
 };
-__device__ __forceinline__ bool unit_pos(const BwdArgs& a, UnitPos& p) {
+template <typename Args>
+__device__ __forceinline__ bool unit_pos(const Args& a, UnitPos& p) {
   const uint32_t wg = blockIdx.x;
   const uint32_t jj = wg >> 3;
   p.chunk = jj % a.nchunks;
@@ -54,8 +55,8 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-template <int D, bool CUT>
-__global__ __launch_bounds__(256) void bwd_dq_f32(BwdArgs a) {
+template <int D, bool CUT, typename Args = BwdArgs>
+__global__ __launch_bounds__(256) void bwd_dq_f32(Args a) {
   typedef F32Cfg<D> C;
   __shared__ __attribute__((aligned(16))) float ks[RB * D];
   __shared__ __attribute__((aligned(16))) float vs[RB * D];
@@ -148,19 +149,17 @@ __global__ __launch_bounds__(256) void bwd_dq_f32(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < C::DL; i += 4) {
       float4 x = make_float4(dq[i] * a.scale, dq[i + 1] * a.scale, dq[i + 2] * a.scale, dq[i + 3] * a.scale);
-      if (a.final_pass) {
+      if (a.final_pass != kAccWrite) {
         const float4 y = *(const float4*)(acc + i);
         x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
-        *(float4*)((float*)a.dq + base + off + i) = x;
-      } else {
-        *(float4*)(acc + i) = x;
       }
+      *(float4*)((a.final_pass == kAccFinal ? (float*)a.dq + base + off : acc) + i) = x;
     }
   }
 }
 
-template <int D, bool CUT>
-__global__ __launch_bounds__(256) void bwd_dkv_f32(BwdArgs a) {
+template <int D, bool CUT, typename Args = BwdArgs>
+__global__ __launch_bounds__(256) void bwd_dkv_f32(Args a) {
   typedef F32Cfg<D> C;
   __shared__ __attribute__((aligned(16))) float qs[RB * D];
   __shared__ __attribute__((aligned(16))) float ds_[RB * D];
@@ -258,36 +257,45 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < C::DL; e += 4) {
       float4 x = make_float4(dk[e] * a.scale, dk[e + 1] * a.scale, dk[e + 2] * a.scale, dk[e + 3] * a.scale);
-      if (a.final_pass) {
+      if (a.final_pass != kAccWrite) {
         const float4 y = *(const float4*)(acc + e);
         x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
-        *(float4*)((float*)a.dk + kbase + koff + e) = x;
-      } else {
-        *(float4*)(acc + e) = x;
       }
+      *(float4*)((a.final_pass == kAccFinal ? (float*)a.dk + kbase + koff : acc) + e) = x;
       *(float4*)(vrow + e) = make_float4(dv[e], dv[e + 1], dv[e + 2], dv[e + 3]);
     }
   }
 }
 
-template <int D>
-hipError_t launch(const BwdArgs& a, bool kind_b, hipStream_t stream) {
+template <int D, typename Args>
+hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 grid((uint32_t)blocks), block(256);
-  if (kind_b) {
-    if (a.cut.on) hipLaunchKernelGGL((bwd_dkv_f32<D, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkv_f32<D, false>), grid, block, 0, stream, a);
-  } else {
-    if (a.cut.on) hipLaunchKernelGGL((bwd_dq_f32<D, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_f32<D, false>), grid, block, 0, stream, a);
+  if constexpr (std::is_same<Args, BwdArgs>::value) {
+    if (a.cut.on) {
+      if (kind_b) hipLaunchKernelGGL((bwd_dkv_f32<D, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_f32<D, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  } else if (a.cut.on) {
+    return hipErrorInvalidValue;
   }
+  if (kind_b) hipLaunchKernelGGL((bwd_dkv_f32<D, false, Args>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dq_f32<D, false, Args>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_f32(BwdArgs a, int head_dim, bool kind_b, hipStream_t stream) {
+  a.nchunks = (a.L + PB - 1) / PB;
+  if (head_dim == 128) return launch<128>(a, kind_b, stream);
+  if (head_dim == 64) return launch<64>(a, kind_b, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_f32_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream) {
   a.nchunks = (a.L + PB - 1) / PB;
   if (head_dim == 128) return launch<128>(a, kind_b, stream);
   if (head_dim == 64) return launch<64>(a, kind_b, stream);

@@ -774,11 +774,13 @@ size_t squad_kpass_workspace_size(const int32_t grid[3], const int32_t* tiles, i
   return levels > 2 ? 2 * one : one;
 }
 
-int squad_kpass_forward(const void* q, const void* k, const void* v, const int32_t grid[3],
-                        const int32_t* tiles, int32_t levels, int32_t heads, void* out, int32_t batch,
-                        int32_t head_dim, int32_t dtype, float scale, void* workspace,
-                        size_t workspace_bytes, squad_stream_t stream) {
-  KGeo kg;
+}  // extern "C"
+
+namespace {
+
+// Shape checks of the k-level entry points.
+int kpass_check(const int32_t grid[3], const int32_t* tiles, int32_t levels, int32_t heads, int32_t batch,
+                int32_t head_dim, int32_t dtype, KGeo& kg) {
   int st = make_kgeo(grid, tiles, levels, kg);
   if (st) return st;
   st = check_common(heads, batch, head_dim, dtype);
@@ -787,39 +789,45 @@ int squad_kpass_forward(const void* q, const void* k, const void* v, const int32
   if ((uint64_t)kg.n * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   for (int j = 0; j < levels; ++j)
     if (too_many_units(bh, (uint64_t)(kg.n / kpass_rows(kg, j)), bh * (uint64_t)kg.n)) return SQUAD_ERR_SHAPE;
-  const size_t bytes = (size_t)bh * kg.n * head_dim * elem_bytes(dtype);
-  const void* in[3] = {q, k, v};
-  st = check_ptrs(in, 3, out, bytes);
-  if (st) return st;
-  const size_t one = (size_t)bh * kg.n * head_dim * (dtype == SQUAD_DTYPE_BF16 ? 2 : 4);
-  const size_t need = levels > 2 ? 2 * one : one;
-  if (!workspace || workspace_bytes < need) return SQUAD_ERR_WORKSPACE;
-  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
-  for (int i = 0; i < 3; ++i)
-    if (overlap(in[i], bytes, workspace, need)) return SQUAD_ERR_ALIAS;
-  if (overlap(out, bytes, workspace, need)) return SQUAD_ERR_ALIAS;
-  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  return SQUAD_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* buf[2] = {(char*)workspace, (char*)workspace + one};
+// Level j's token maps when it is the first or the last level: the two-pass
+// operator's local pass (tile = the level-1 tile) or global pass (tile = the
+// level-(k-1) tile).
+int kpass_end_map(const KGeo& kg, const int32_t grid[3], int j, int32_t heads, int32_t head_dim, RowMap& m) {
+  Geo g;
+  const int ti = j == 0 ? 1 : kg.k - 1;
+  const int32_t tile[3] = {(int32_t)kg.ext[ti][0], (int32_t)kg.ext[ti][1], (int32_t)kg.ext[ti][2]};
+  const int st = make_geo(grid, tile, g);
+  if (st) return st;
+  m = token_map(g, heads, head_dim, j == 0);
+  return SQUAD_OK;
+}
+
+// The k levels of the forward: level j reads its values from v (j = 0) or
+// level_out[j - 1] and writes level_out[j] (out for the last level); lse_base
+// (optional) receives each level's row statistics, batch*heads*n floats per level.
+int kpass_levels_forward(const void* q, const void* k, const void* v, const KGeo& kg, const int32_t grid[3],
+                         int32_t heads, void* out, int32_t batch, int32_t head_dim, int32_t dtype, float scale,
+                         void* const* level_out, float* lse_base, hipStream_t s) {
+  const int levels = kg.k;
+  const size_t rows = (size_t)heads * batch * kg.n;
   const bool bf16 = dtype == SQUAD_DTYPE_BF16;
   for (int j = 0; j < levels; ++j) {
     const uint32_t L = (uint32_t)kpass_rows(kg, j);
     const uint32_t U = (uint32_t)(kg.n / L);
-    const void* vin = j == 0 ? v : buf[(j - 1) & 1];
-    void* o = j == levels - 1 ? out : buf[j & 1];
+    const void* vin = j == 0 ? v : level_out[j - 1];
+    void* o = j == levels - 1 ? out : level_out[j];
+    float* lse = lse_base ? lse_base + (size_t)j * rows : nullptr;
+    int st;
     if (j == 0 || j == levels - 1) {
-      // the first and last levels are the two-pass operator's local pass (tile =
-      // the level-1 tile) and global pass (tile = the level-(k-1) tile)
-      Geo g;
-      const int ti = j == 0 ? 1 : levels - 1;
-      const int32_t tile[3] = {(int32_t)kg.ext[ti][0], (int32_t)kg.ext[ti][1], (int32_t)kg.ext[ti][2]};
-      st = make_geo(grid, tile, g);
-      if (st) return st;
       AttnArgs a = attn_args(q, k, vin, o, L, U, heads, batch, head_dim, scale);
-      a.mqk = token_map(g, heads, head_dim, j == 0);
+      st = kpass_end_map(kg, grid, j, heads, head_dim, a.mqk);
+      if (st) return st;
       a.mv = a.mqk;
       a.mo = a.mqk;
+      a.lse = lse;
       const VType vt = j == 0 ? VType::kBf16ToF16 : VType::kF16ToBf16;
       st = run_attn(a, head_dim, dtype, s, vt);
     } else {
@@ -833,9 +841,200 @@ int squad_kpass_forward(const void* q, const void* k, const void* v, const int32
       a.mv = a.mqk;
       a.mo = a.mqk;
       a.v_like_k = 1;
+      a.lse = lse;
       if (a.units == 0) continue;
       const hipError_t e = bf16 ? launch_attn_bf16_k(a, head_dim, s) : launch_attn_f32_k(a, head_dim, s);
       st = e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+    }
+    if (st) return st;
+  }
+  return SQUAD_OK;
+}
+
+// Training workspace of k levels (sections 256-byte aligned): the intermediate
+// outputs o_1 .. o_(k-1) (fp16 for bf16 calls), each level's row statistics, D,
+// two buffers for the intermediate outputs' gradients (the call's dtype), and for
+// bf16 calls the fp32 sums of dq and dk.
+struct KTrainLayout {
+  size_t inter, lse, dsum, dgrad[2], dq_acc, dk_acc, one_i, one_g, total;
+};
+
+KTrainLayout kpass_train_layout(const KGeo& kg, int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)heads * batch * kg.n;
+  const bool bf16 = dtype == SQUAD_DTYPE_BF16;
+  KTrainLayout t;
+  t.one_i = al(rows * head_dim * (bf16 ? 2 : 4));
+  t.one_g = al(rows * head_dim * elem_bytes(dtype));
+  t.inter = 0;
+  t.lse = t.inter + (size_t)(kg.k - 1) * t.one_i;
+  t.dsum = al(t.lse + (size_t)kg.k * rows * 4);
+  t.dgrad[0] = al(t.dsum + rows * 4);
+  t.dgrad[1] = t.dgrad[0] + t.one_g;
+  size_t end = t.dgrad[1] + t.one_g;
+  t.dq_acc = t.dk_acc = 0;
+  if (bf16) {
+    t.dq_acc = end;
+    t.dk_acc = al(t.dq_acc + rows * head_dim * 4);
+    end = al(t.dk_acc + rows * head_dim * 4);
+  }
+  t.total = end;
+  return t;
+}
+
+template <typename Args>
+void kpass_bwd_common(Args& a, const KGeo& kg, int j, int32_t heads, int32_t batch, int32_t head_dim, float scale) {
+  a.L = (uint32_t)kpass_rows(kg, j);
+  a.U = (uint32_t)(kg.n / a.L);
+  a.heads = (uint32_t)heads;
+  a.BH = (uint32_t)(heads * batch);
+  a.fBH = FastDiv(a.BH);
+  a.fHeads = FastDiv(a.heads);
+  a.units = a.BH * a.U;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)head_dim);
+  a.scale = (float)sc;
+  a.c = (float)(sc * 1.4426950408889634);
+}
+
+}  // namespace
+
+extern "C" {
+
+int squad_kpass_forward(const void* q, const void* k, const void* v, const int32_t grid[3],
+                        const int32_t* tiles, int32_t levels, int32_t heads, void* out, int32_t batch,
+                        int32_t head_dim, int32_t dtype, float scale, void* workspace,
+                        size_t workspace_bytes, squad_stream_t stream) {
+  KGeo kg;
+  int st = kpass_check(grid, tiles, levels, heads, batch, head_dim, dtype, kg);
+  if (st) return st;
+  const uint64_t bh = (uint64_t)heads * (uint64_t)batch;
+  const size_t bytes = (size_t)bh * kg.n * head_dim * elem_bytes(dtype);
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  const size_t one = (size_t)bh * kg.n * head_dim * (dtype == SQUAD_DTYPE_BF16 ? 2 : 4);
+  const size_t need = levels > 2 ? 2 * one : one;
+  if (!workspace || workspace_bytes < need) return SQUAD_ERR_WORKSPACE;
+  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i)
+    if (overlap(in[i], bytes, workspace, need)) return SQUAD_ERR_ALIAS;
+  if (overlap(out, bytes, workspace, need)) return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  // intermediate outputs alternate between two buffers
+  void* level_out[KMAX];
+  for (int j = 0; j < levels; ++j) level_out[j] = (char*)workspace + (j & 1) * one;
+  return kpass_levels_forward(q, k, v, kg, grid, heads, out, batch, head_dim, dtype, scale, level_out, nullptr,
+                              (hipStream_t)stream);
+}
+
+size_t squad_kpass_train_workspace_size(const int32_t grid[3], const int32_t* tiles, int32_t levels,
+                                        int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
+  KGeo kg;
+  if (kpass_check(grid, tiles, levels, heads, batch, head_dim, dtype, kg)) return 0;
+  return kpass_train_layout(kg, heads, batch, head_dim, dtype).total;
+}
+
+int squad_kpass_forward_train(const void* q, const void* k, const void* v, const int32_t grid[3],
+                              const int32_t* tiles, int32_t levels, int32_t heads, void* out, int32_t batch,
+                              int32_t head_dim, int32_t dtype, float scale, void* workspace,
+                              size_t workspace_bytes, squad_stream_t stream) {
+  KGeo kg;
+  int st = kpass_check(grid, tiles, levels, heads, batch, head_dim, dtype, kg);
+  if (st) return st;
+  const size_t bytes = (size_t)heads * batch * kg.n * head_dim * elem_bytes(dtype);
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  const KTrainLayout t = kpass_train_layout(kg, heads, batch, head_dim, dtype);
+  if (!workspace || workspace_bytes < t.total) return SQUAD_ERR_WORKSPACE;
+  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i)
+    if (overlap(in[i], bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  if (overlap(out, bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  char* ws = (char*)workspace;
+  void* level_out[KMAX];
+  for (int j = 0; j + 1 < levels; ++j) level_out[j] = ws + t.inter + (size_t)j * t.one_i;
+  return kpass_levels_forward(q, k, v, kg, grid, heads, out, batch, head_dim, dtype, scale, level_out,
+                              (float*)(ws + t.lse), (hipStream_t)stream);
+}
+
+int squad_kpass_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const int32_t grid[3], const int32_t* tiles, int32_t levels, int32_t heads, void* dq,
+                         void* dk, void* dv, int32_t batch, int32_t head_dim, int32_t dtype, float scale,
+                         void* workspace, size_t workspace_bytes, squad_stream_t stream) {
+  KGeo kg;
+  int st = kpass_check(grid, tiles, levels, heads, batch, head_dim, dtype, kg);
+  if (st) return st;
+  const size_t bytes = (size_t)heads * batch * kg.n * head_dim * elem_bytes(dtype);
+  const void* in[5] = {q, k, v, out, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (const void* p : in)
+    if (!p) return SQUAD_ERR_INVALID_ARG;
+  for (const void* p : outs)
+    if (!p) return SQUAD_ERR_INVALID_ARG;
+  if (!workspace) return SQUAD_ERR_WORKSPACE;
+  for (const void* p : in)
+    if (misaligned(p)) return SQUAD_ERR_ALIGN;
+  for (const void* p : outs)
+    if (misaligned(p)) return SQUAD_ERR_ALIGN;
+  if (misaligned(workspace)) return SQUAD_ERR_ALIGN;
+  const KTrainLayout t = kpass_train_layout(kg, heads, batch, head_dim, dtype);
+  if (workspace_bytes < t.total) return SQUAD_ERR_WORKSPACE;
+  for (int i = 0; i < 3; ++i) {
+    for (const void* p : in)
+      if (overlap(outs[i], bytes, p, bytes)) return SQUAD_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], bytes, outs[j], bytes)) return SQUAD_ERR_ALIAS;
+    if (overlap(outs[i], bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  }
+  for (const void* p : in)
+    if (overlap(p, bytes, workspace, t.total)) return SQUAD_ERR_ALIAS;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == SQUAD_DTYPE_BF16;
+  const size_t rows = (size_t)heads * batch * kg.n;
+  float* dq_acc = bf16 ? (float*)(ws + t.dq_acc) : (float*)dq;
+  float* dk_acc = bf16 ? (float*)(ws + t.dk_acc) : (float*)dk;
+  auto inter = [&](int j) -> void* { return ws + t.inter + (size_t)(j - 1) * t.one_i; };   // o_j, j >= 1
+  // from the last level down: level j's values are o_j (v for j = 0), its output
+  // o_(j+1) (out for the last), its upstream gradient that of o_(j+1) (dout for
+  // the last); it adds its parts of dq and dk and writes the gradient of o_j
+  for (int j = levels - 1; j >= 0; --j) {
+    const void* vals = j == 0 ? v : inter(j);
+    const void* outj = j == levels - 1 ? out : inter(j + 1);
+    const void* up = j == levels - 1 ? dout : ws + t.dgrad[(j + 1) & 1];
+    void* dvj = j == 0 ? dv : ws + t.dgrad[j & 1];
+    const uint32_t mode = j == levels - 1 ? kAccWrite : (j == 0 ? kAccFinal : kAccAdd);
+    auto fill = [&](auto& a) {
+      kpass_bwd_common(a, kg, j, heads, batch, head_dim, scale);
+      a.q = q; a.k = k; a.v = vals; a.o = outj; a.dout = up;
+      a.mv = a.mqk; a.mo = a.mqk; a.mdo = a.mqk; a.mdq = a.mqk; a.mdk = a.mqk; a.mdv = a.mqk;
+      a.lse = (const float*)(ws + t.lse) + (size_t)j * rows;
+      a.dsum = (float*)(ws + t.dsum);
+      a.dq = dq; a.dk = dk; a.dq_acc = dq_acc; a.dk_acc = dk_acc; a.dv = dvj;
+      a.final_pass = mode;
+    };
+    if (j == 0 || j == levels - 1) {
+      BwdArgs a;
+      memset(&a, 0, sizeof(a));
+      st = kpass_end_map(kg, grid, j, heads, head_dim, a.mqk);
+      if (st) return st;
+      fill(a);
+      st = run_bwd(a, head_dim, dtype, BwdTypes{j >= 1, j < levels - 1}, s);
+    } else {
+      BwdArgsK a;
+      memset(&a, 0, sizeof(a));
+      a.mqk = kpass_map(kg, j, heads, head_dim);
+      fill(a);
+      if (a.units == 0) continue;
+      for (int kind = 0; kind < 2 && !st; ++kind) {
+        const hipError_t e = bf16 ? launch_bwd_bf16_k(a, head_dim, kind == 1, s)
+                                  : launch_bwd_f32_k(a, head_dim, kind == 1, s);
+        st = e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+      }
     }
     if (st) return st;
   }

@@ -85,17 +85,20 @@ hipError_t launch_attn_f32_k(AttnArgsK a, int head_dim, hipStream_t stream);
 //   kind A (per query row i):  D_i = <dout_i, o_i>;  dq_i = scale * sum_j dS_ij k_j
 //   kind B (per key row j):    dv_j = sum_i P_ij dout_i;  dk_j = scale * sum_i dS_ij q_i
 // with P_ij = exp2(c <q_i, k_j> - lse_i) and dS_ij = P_ij (<dout_i, v_j> - D_i).
-// Kind A writes D (dsum) for kind B.  dq and dk are summed over the two passes:
-// the first pass writes its part to the fp32 accumulators (token order, the
-// offsets of mdq / mdk); the second adds them and writes dq / dk in the call's
-// dtype (for fp32 calls the accumulators may be dq and dk themselves).
-struct BwdArgs {
+// Kind A writes D (dsum) for kind B.  dq and dk are summed over the passes: the
+// first pass writes its part to the fp32 accumulators (token order, the offsets
+// of mdq / mdk), middle passes (k levels) add to them, and the last adds them and
+// writes dq / dk in the call's dtype (for fp32 calls the accumulators may be dq
+// and dk themselves).
+enum BwdAcc : uint32_t { kAccWrite = 0, kAccFinal = 1, kAccAdd = 2 };
+template <typename Map>
+struct BwdArgsT {
   const void* q;
   const void* k;
   const void* v;      // value rows (the global pass: the local output)
   const void* o;      // this pass's output rows (kind A, for D)
   const void* dout;   // upstream gradient of this pass's output
-  RowMap mqk, mv, mo, mdo;
+  Map mqk, mv, mo, mdo;
   const float* lse;   // [u * L + r]
   float* dsum;        // [u * L + r]: D, written by kind A, read by kind B
   void* dq;           // kind A, final pass: dq in the call's dtype (token order, mdq)
@@ -103,8 +106,8 @@ struct BwdArgs {
   float* dq_acc;      // fp32 accumulators (mdq / mdk offsets)
   float* dk_acc;
   void* dv;           // kind B: value gradient rows (mdv)
-  RowMap mdq, mdk, mdv;
-  uint32_t final_pass;  // 0: write the accumulators; 1: add them, write dq / dk
+  Map mdq, mdk, mdv;
+  uint32_t final_pass;  // BwdAcc: write the accumulators / add them and write dq, dk / add to them
   uint32_t L, U, heads, BH;
   FastDiv fBH, fHeads;
   uint32_t units, nchunks;
@@ -112,6 +115,8 @@ struct BwdArgs {
   float scale;
   Cut cut;
 };
+typedef BwdArgsT<RowMap> BwdArgs;
+typedef BwdArgsT<RowMapK> BwdArgsK;   // middle levels of a k-level operator
 
 // Element types of the bf16 engine's backward launches (q, k, dout and the
 // gradients are bf16; o and v may be the fp16 local output).
@@ -121,11 +126,14 @@ struct BwdTypes {
 };
 
 hipError_t launch_bwd_f32(BwdArgs a, int head_dim, bool kind_b, hipStream_t stream);
+hipError_t launch_bwd_f32_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream);
 
 // The measuring kernel: blocks x 256 threads, each wave `iters` rounds of four
 // independent 32x32x16 bf16 MFMAs; out[blocks * 256] receives a checksum per lane.
 hipError_t launch_mfma_probe(float* out, int32_t blocks, int32_t iters, hipStream_t stream);
 hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hipStream_t stream);
+// middle levels: fp16 values and outputs
+hipError_t launch_bwd_bf16_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream);
 
 // Row-permutation copy: rows e = (bh * U + s) * L + r for bh < BH, s < U, r < L;
 // row e is read at src + ms(b, h, s, r) and written at dst + md(b, h, s, r).

@@ -364,3 +364,27 @@ def test_block_entry_point_rejects_bad_arguments():
     assert blk(grid=_lib.int3((64, 48, 80)), d=128, heads=24, wb=1 << 40) == SHAPE
     assert sq.squad_block_workspace_size((64, 48, 80), (4, 12, 10), 24, 1, 128, 1) == 0
     assert sq.squad_block_workspace_size((32, 24, 40), (2, 8, 10), 24, 1, 128, 1) > 0
+
+
+def test_kpass_training_argument_checks():
+    lib = _lib.lib()
+    p = ctypes.c_void_p
+    assert sq.squad_kpass_train_workspace_size((4, 8, 8), [(1, 4, 4), (2, 2, 8)], 2, 1, 64, 1) == 0   # not nested
+    need = sq.squad_kpass_train_workspace_size((4, 8, 8), [(1, 2, 2), (2, 4, 4)], 2, 1, 64, 1)
+    # two fp16 intermediates, three levels of statistics, D, two gradient buffers, two fp32 sums
+    assert need >= 2 * 256 * 2 * 64 * 2 + 4 * 256 * 2 * 4 + 2 * 256 * 2 * 64 * 2 + 2 * 256 * 2 * 64 * 4
+    arr = (ctypes.c_int32 * 6)(1, 2, 2, 2, 4, 4)
+    g = _lib.int3((4, 8, 8))
+    D, K, V, OUT, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+    def bwd(dq=D, ws=WS, wb=1 << 30, levels=3):
+        return lib.squad_kpass_backward(p(A), p(B), p(C), p(OUT), p(DOUT), g, arr, levels, 2, p(dq), p(K), p(V), 1,
+                                        64, 1, ctypes.c_float(0), p(ws), wb, None)
+    assert bwd(levels=1) == INVALID
+    assert bwd(dq=A) == ALIAS
+    assert bwd(ws=0) == WORKSPACE
+    assert bwd(wb=need - 1) == WORKSPACE
+    assert lib.squad_kpass_forward_train(p(A), p(B), p(C), g, arr, 3, 2, p(O), 1, 64, 1, ctypes.c_float(0), p(WS),
+                                         need - 1, None) == WORKSPACE
+    if _device_count() == 0:
+        assert bwd() == HIP

@@ -101,3 +101,53 @@ def test_kpass_at_highres_size_properties():
     assert float((outc.float() - vc.float()).abs().max()) <= 1.5e-2
     mean = v.double().mean(dim=1, keepdim=True)
     assert float((outz.double() - mean).abs().max()) <= 1.5e-2
+
+
+# ---------------------------------------------------------------- k-level training
+
+KBWD_CASES = [
+    ((4, 8, 8), [(1, 2, 2), (2, 4, 4)], 1, 2, 64, torch.float32),
+    ((4, 8, 8), [(1, 2, 2), (2, 4, 4)], 2, 2, 128, torch.bfloat16),
+    ((4, 4, 8), [(1, 2, 2), (2, 2, 4), (2, 4, 8)], 1, 2, 128, torch.bfloat16),   # two middle levels
+    ((8, 16, 20), [(2, 4, 5), (4, 8, 10)], 1, 2, 128, torch.bfloat16),
+    ((4, 6, 10), [(1, 3, 5), (2, 6, 10)], 1, 2, 64, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", KBWD_CASES, ids=lambda c: f"{c[0]}-k{len(c[1]) + 1}-d{c[4]}-{str(c[5])[6:]}")
+def test_kpass_backward_matches_oracle(case):
+    grid, tiles, B, Hh, d, dtype = case
+    n = grid[0] * grid[1] * grid[2]
+    q, k, v = rand_inputs((B, n, Hh, d), dtype, 45)
+    g = torch.Generator().manual_seed(46)
+    dout = torch.randn(B, n, Hh, d, generator=g).to(dtype).cuda()
+    say(f"kpass backward {case}")
+    out, ws = sq.squad_kpass_forward_train(q, k, v, grid, tiles)
+    grads = sq.squad_kpass_backward(q, k, v, out, dout, grid, tiles, ws)
+    ref = sq.squad_kpass_forward(q, k, v, grid, tiles)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    want = oracle.squad_kpass_backward(f64(q), f64(k), f64(v), f64(dout), grid, tiles)
+    tol = 1e-4 if dtype == torch.float32 else 2.5e-2
+    for name, got, w in zip(("dq", "dk", "dv"), grads, want):
+        err = float(np.max(np.abs(f64(got) - w)))
+        bound = tol * max(1.0, float(np.max(np.abs(w))))
+        say(f"  {name}: max-abs {err:.3e} (bound {bound:.3e})")
+        assert np.isfinite(f64(got)).all() and err <= bound
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_kpass_backward_two_levels_is_the_two_pass_backward(dtype):
+    """Two levels run the same kernels as squad_attn_backward with the local output
+    in token order instead of group-major: the same bits."""
+    grid, tile = (4, 6, 10), (2, 3, 5)
+    q, k, v = rand_inputs((2, 240, 2, 128), dtype, 47)
+    dout = torch.randn(2, 240, 2, 128, generator=torch.Generator().manual_seed(48)).to(dtype).cuda()
+    out, ws = sq.squad_kpass_forward_train(q, k, v, grid, [tile])
+    a = sq.squad_kpass_backward(q, k, v, out, dout, grid, [tile], ws)
+    out2, ws2 = sq.squad_attn_forward_train(q, k, v, grid, tile)
+    b = sq.squad_attn_backward(q, k, v, out2, dout, grid, tile, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
