@@ -395,9 +395,25 @@ def kpass_rates(sq, q, k, v, heads, stream):
     ms = time_launches(fwd, stream, 20)
     n = grid[0] * grid[1] * grid[2]
     flops = 4.0 * q.shape[-1] * (64 + 64 + 60) * n * heads
-    del out, ws
+    del ws
+    # training: the forward keeping its state, then the gradients
+    tws = torch.empty(sq.squad_kpass_train_workspace_size(grid, tiles, heads, 1, q.shape[-1], q.dtype),
+                      dtype=torch.uint8, device=q.device)
+    dout = torch.randn(q.shape, generator=torch.Generator(device=q.device).manual_seed(78), device=q.device,
+                       dtype=torch.float32).to(q.dtype)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ftrain = lambda: sq.squad_kpass_forward_train(q, k, v, grid, tiles, heads, out=out, workspace=tws, stream=stream)
+    bwd = lambda: sq.squad_kpass_backward(q, k, v, out, dout, grid, tiles, tws, heads, dq=grads[0], dk=grads[1],
+                                          dv=grads[2], stream=stream)
+    ftrain()
+    bwd()
+    torch.cuda.synchronize()
+    ms_ft = time_launches(ftrain, stream, 10)
+    ms_b = time_launches(bwd, stream, 10)
+    del out, tws, dout, grads
     return {"grid": list(grid), "tiles": [list(t) for t in tiles], "levels": 3, "unit_rows": [64, 64, 60],
-            "ms": round(ms, 4), "tokens_per_s": round(n / (ms * 1e-3), 1), "tflops": round(flops / ms / 1e9, 1)}
+            "ms": round(ms, 4), "tokens_per_s": round(n / (ms * 1e-3), 1), "tflops": round(flops / ms / 1e9, 1),
+            "forward_train_ms": round(ms_ft, 4), "backward_ms": round(ms_b, 4)}
 
 
 def present_pairs(grid, tile):
