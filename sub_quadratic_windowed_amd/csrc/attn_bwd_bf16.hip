@@ -50,11 +50,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BN = 32;   // rows per streamed block
-constexpr int NW = 4;    // waves per workgroup
-constexpr int BM = 32 * NW;
 
-template <int D>
+// NW waves per workgroup (4, or 2 for units of at most 64 rows), 32 own rows each
+template <int D, int NW>
 struct BCfg {
+  static constexpr int BM = 32 * NW;             // own rows per workgroup
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int GRP = 4 * D;             // elements of one 4-row group
   static constexpr int GPI = 64 / (4 * CPR);    // groups filled by one direct load
@@ -134,9 +134,9 @@ struct StatStage {
 };
 
 // Per-lane geometry of the grouped layout.
-template <int D>
+template <int D, int NW>
 struct Layout {
-  typedef BCfg<D> C;
+  typedef BCfg<D, NW> C;
   // direct loads: lane i of load `ins` fills slot i of its groups
   uint32_t ld_row[C::VPW];      // row within the block
   uint32_t ld_byte[C::VPW];     // byte offset of the chunk within the row
@@ -169,16 +169,15 @@ struct Layout {
 };
 
 // A operand from rows: 32 rows x dims 16 kk ... (lane: row l32, chunk 2 kk + half)
-template <int D, bool F16>
-__device__ __forceinline__ bf16x8 read_rows(const char* stage, const Layout<D>& lay, int kk) {
+template <bool F16, typename Lay>
+__device__ __forceinline__ bf16x8 read_rows(const char* stage, const Lay& lay, int kk) {
   return frag<F16>(*(const uint4*)(stage + lay.rd[kk & 1] + 256 * (kk >> 1)));
 }
 
 // A operand transposed: dims 32 mt + (lane % 32) x rows 16 jk + (permuted)
-template <int D, bool F16>
-__device__ __forceinline__ bf16x8 read_tr(const char* stage, const Layout<D>& lay, int jk, int mt) {
-  typedef BCfg<D> C;
-  const char* p = stage + 2 * (4 * jk * C::GRP + 128 * mt);
+template <int D, bool F16, typename Lay>
+__device__ __forceinline__ bf16x8 read_tr(const char* stage, const Lay& lay, int jk, int mt) {
+  const char* p = stage + 2 * (4 * jk * (4 * D) + 128 * mt);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p + lay.tr_lo));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p + lay.tr_hi));
   // the two halves side by side: a register pairing, no arithmetic
@@ -241,9 +240,10 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
 
 // ---------------------------------------------------------------- kind A: dq (and D)
 
-template <int D, bool VF16, bool OF16, bool CUT, bool TAB, typename Args = BwdArgs>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(Args a) {
-  typedef BCfg<D> C;
+template <int D, int NW, bool VF16, bool OF16, bool CUT, bool TAB, typename Args = BwdArgs>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(Args a) {
+  typedef BCfg<D, NW> C;
+  constexpr int BM = C::BM;
   UnitPos p;
   if (!unit_pos(a, p)) return;
   const uint32_t tid = threadIdx.x;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const float lse = qok ? a.lse[row_id] : 0.f;
   if (qok && half == 0) a.dsum[row_id] = dsum;
 
-  Layout<D> lay;
+  Layout<D, NW> lay;
   lay.init(lane, wave);
   const uint32_t nkb = (L + BN - 1) / BN;
   int32_t* tab = RowTab<TAB>::ptr();   // K rows, then V rows (byte offsets)
@@ -375,12 +375,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        sc = mfma(read_rows<D, false>(ks, lay, kk), qf[kk], sc);
+        sc = mfma(read_rows<false>(ks, lay, kk), qf[kk], sc);
         if constexpr (VF16)
           dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               __builtin_bit_cast(f16x8l, *(const uint4*)(vs + lay.rd[kk & 1] + 256 * (kk >> 1))), dh[kk], dp, 0, 0, 0);
         else
-          dp = mfma(read_rows<D, false>(vs, lay, kk), df[kk], dp);
+          dp = mfma(read_rows<false>(vs, lay, kk), df[kk], dp);
       }
       // present keys of the block: bit j for key kb * 32 + j, then this half's bits
       uint32_t km = 0xffffffffu;
@@ -444,9 +444,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 // ---------------------------------------------------------------- kind B: dk, dv
 
-template <int D, bool VF16, bool CUT, bool TAB, typename Args = BwdArgs>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(Args a) {
-  typedef BCfg<D> C;
+template <int D, int NW, bool VF16, bool CUT, bool TAB, typename Args = BwdArgs>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(Args a) {
+  typedef BCfg<D, NW> C;
+  constexpr int BM = C::BM;
   UnitPos p;
   if (!unit_pos(a, p)) return;
   const uint32_t tid = threadIdx.x;
@@ -481,10 +482,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   // holding them in registers instead would not leave room for both accumulators
   __shared__ __attribute__((aligned(1024))) __bf16 vown[BM * D];
   {
-    constexpr int PER = BM * C::CPR / 256;
+    constexpr int PER = BM * C::CPR / (64 * NW);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t ch = tid + 256 * i;
+      const uint32_t ch = tid + 64 * NW * i;
       const uint32_t r = ch / C::CPR, cc = ch % C::CPR;
       const uint32_t vr = load_row(p.chunk * BM + r);
       const uint4 raw = *(const uint4*)(vg + 2 * a.mv.row_off(vr) + 16 * cc);
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   const char* vrow_lds = (const char*)vown + (wave * 32 + l32) * D * 2;
   const uint32_t vxor = l32 & (C::CPR - 1);
 
-  Layout<D> lay;
+  Layout<D, NW> lay;
   lay.init(lane, wave);
   const size_t unit_rows = (size_t)p.u * L;
   const uint32_t nqb = (L + BN - 1) / BN;
@@ -572,8 +573,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        sc = mfma(read_rows<D, false>(qs, lay, kk), kf[kk], sc);
-        dp = mfma(read_rows<D, false>(ds, lay, kk),
+        sc = mfma(read_rows<false>(qs, lay, kk), kf[kk], sc);
+        dp = mfma(read_rows<false>(ds, lay, kk),
                   *(const bf16x8*)(vrow_lds + (((uint32_t)(2 * kk) + half) ^ vxor) * 16), dp);
       }
       bf16x8 pb[2], sb[2];
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   }
 }
 
-template <int D, bool VF16, bool OF16, typename Args>
+template <int D, int NW, bool VF16, bool OF16, typename Args>
 hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
@@ -640,46 +641,50 @@ hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
     // (the host allows cut tilings only where the units fit the row tables)
     if (a.cut.on) {
       if (a.L > BT_ROWS) return hipErrorInvalidValue;
-      if (kind_b) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, true, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, true, true>), grid, block, 0, stream, a);
+      if (kind_b) hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, true, true>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   } else if (a.cut.on) {
     return hipErrorInvalidValue;
   }
   if (kind_b) {
-    if (a.L <= BT_ROWS) hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, true, Args>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkv_bf16<D, VF16, false, false, Args>), grid, block, 0, stream, a);
+    if (a.L <= BT_ROWS)
+      hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, false, true, Args>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, false, false, Args>), grid, block, 0, stream, a);
   } else {
     if (a.L <= BT_ROWS)
-      hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, true, Args>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, false, true, Args>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dq_bf16<D, VF16, OF16, false, false, Args>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, false, false, Args>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_types(const BwdArgs& a, BwdTypes t, bool kind_b, hipStream_t stream) {
-  if (t.v_f16 && !t.o_f16) return launch<D, true, false>(a, kind_b, stream);
-  if (!t.v_f16 && t.o_f16) return launch<D, false, true>(a, kind_b, stream);
+// Waves per workgroup: 2 for units of at most 64 rows (half of a 4-wave
+// workgroup would idle on them), else 4.
+template <bool VF16, bool OF16, typename Args>
+hipError_t launch_nw(Args a, int head_dim, bool kind_b, hipStream_t stream) {
+  const int nw = a.L <= 64 ? 2 : 4;
+  a.nchunks = (a.L + 32 * nw - 1) / (32 * nw);
+  if (head_dim == 128)
+    return nw == 2 ? launch<128, 2, VF16, OF16>(a, kind_b, stream) : launch<128, 4, VF16, OF16>(a, kind_b, stream);
+  if (head_dim == 64)
+    return nw == 2 ? launch<64, 2, VF16, OF16>(a, kind_b, stream) : launch<64, 4, VF16, OF16>(a, kind_b, stream);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hipStream_t stream) {
-  a.nchunks = (a.L + BM - 1) / BM;
-  if (head_dim == 128) return launch_types<128>(a, t, kind_b, stream);
-  if (head_dim == 64) return launch_types<64>(a, t, kind_b, stream);
+  if (t.v_f16 && !t.o_f16) return launch_nw<true, false>(a, head_dim, kind_b, stream);
+  if (!t.v_f16 && t.o_f16) return launch_nw<false, true>(a, head_dim, kind_b, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_bf16_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream) {
-  a.nchunks = (a.L + BM - 1) / BM;
-  if (head_dim == 128) return launch<128, true, true>(a, kind_b, stream);
-  if (head_dim == 64) return launch<64, true, true>(a, kind_b, stream);
-  return hipErrorInvalidValue;
+  return launch_nw<true, true>(a, head_dim, kind_b, stream);
 }
 
 }  // namespace squad
