@@ -64,6 +64,9 @@ BWD_CASES = [
     ((3, 5, 7), (2, 2, 3), 1, 2, 64, torch.float32, False),       # cut tilings
     ((3, 5, 7), (2, 2, 3), 2, 2, 128, torch.bfloat16, True),
     ((5, 12, 20), (2, 5, 6), 1, 2, 128, torch.bfloat16, False),
+    ((4, 8, 8), (1, 8, 8), 1, 2, 128, torch.bfloat16, True),      # W = 64: two-wave workgroups
+    ((5, 13, 4), (5, 13, 1), 1, 2, 128, torch.bfloat16, False),   # W = 65: four-wave, one row past
+    ((4, 8, 8), (1, 8, 8), 1, 2, 64, torch.float32, False),
 ]
 
 
