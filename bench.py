@@ -153,7 +153,20 @@ def cpu_baseline(cfg, qc, kc, vc, heads):
                   f"({cfg.batch}x{cfg.n} tokens, head_dim {cfg.head_dim}); {dt:.1f} s, scaled by "
                   f"{cfg.heads}/{heads} to the whole workload",
         "seconds": dt,
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -281,6 +294,7 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
         base = cpu_baseline(cfg, qc, kc, vc, args.cpu_heads)
+        base["gpu_over_cpu"] = round(tokens_per_s / base["value"], 1)
 
     line = {
         "metric": METRIC,
