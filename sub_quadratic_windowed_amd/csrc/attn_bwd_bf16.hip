@@ -632,6 +632,189 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// ---------------------------------------------------------------- units of at most 64 rows
+
+// A whole unit of at most 64 rows in one two-wave workgroup: S and dP are formed
+// once and feed all three gradients (five products instead of the seven of kinds A
+// and B, and every row read once).  All of the unit's Q, dout, K and V rows sit in
+// LDS (grouped layout, two blocks each).  Wave w owns keys 32 w .. 32 w + 31 as in
+// kind B (S = Q K^T, dP = dout V^T with B = its key rows; dv^T += dout^T P,
+// dk^T += Q^T dS) and writes dS to LDS as rows of queries; once both waves' keys
+// are in, wave w forms dq^T of query block w as K^T dS^T (A = K^T by the
+// transposing read, B = dS^T rows in the key order of that read).  D = <dout, o>
+// of the unit's rows is formed in the prologue, one row per lane pair.
+constexpr int SMALL_ROWS = 64;
+constexpr int DS_PITCH = 2 * BN + 8;   // 16-bit elements per dS row (8 of padding)
+
+template <int D, bool VF16, bool OF16, typename Args>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_small_bf16(Args a) {
+  constexpr int NW = 2;
+  typedef BCfg<D, NW> C;
+  UnitPos p;
+  if (!unit_pos(a, p)) return;   // one workgroup per unit (nchunks = 1)
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t half = lane >> 5, l32 = lane & 31;
+  const uint32_t L = a.L;   // 1 .. 64
+  auto load_row = [&](uint32_t r) -> uint32_t { return min(r, L - 1); };
+  const char* qg = (const char*)a.q + 2 * a.mqk.base(p.b, p.h, p.s);
+  const char* kg = (const char*)a.k + 2 * a.mqk.base(p.b, p.h, p.s);
+  const char* vg = (const char*)a.v + 2 * a.mv.base(p.b, p.h, p.s);
+  const char* og = (const char*)a.o + 2 * a.mo.base(p.b, p.h, p.s);
+  const char* dg = (const char*)a.dout + 2 * a.mdo.base(p.b, p.h, p.s);
+  const uint32_t nb = (L + BN - 1) / BN;   // 1 or 2 blocks
+
+  Layout<D, NW> lay;
+  lay.init(lane, wave);
+  // every row of the unit: Q, dout, K and V blocks by direct loads (rows past the
+  // end read the last row; their scores are masked and their dS is zero)
+  auto issue = [&](uint32_t b, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+#pragma unroll
+    for (int i = 0; i < C::VPW; ++i) {
+      const uint32_t ins = wave + i * NW;
+      const uint32_t r = load_row(b * BN + lay.ld_row[i]);
+      const uint32_t qo = 2 * a.mqk.row_off(r) + lay.ld_byte[i];
+      __builtin_amdgcn_global_load_lds((const void*)(qg + qo), (lds_void_t*)(BStage<D, ST, 2>::ptr() + ins * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kg + qo), (lds_void_t*)(BStage<D, ST, 4>::ptr() + ins * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(dg + 2 * a.mdo.row_off(r) + lay.ld_byte[i]),
+                                       (lds_void_t*)(BStage<D, ST, 3>::ptr() + ins * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg + 2 * a.mv.row_off(r) + lay.ld_byte[i]),
+                                       (lds_void_t*)(BStage<D, ST, 5>::ptr() + ins * 1024), 16, 0, 0);
+    }
+  };
+  issue(0, std::integral_constant<int, 0>{});
+  if (nb > 1) issue(1, std::integral_constant<int, 1>{});
+
+  // row statistics of the unit: lse and D = <dout, o> (wave w: rows 32 w + l32)
+  __shared__ __attribute__((aligned(16))) float stat_l[SMALL_ROWS];
+  __shared__ __attribute__((aligned(16))) float stat_d[SMALL_ROWS];
+  const uint32_t rj = wave * 32 + l32;   // this lane's key (kind-B role) and query (dq)
+  const bool rok = rj < L;
+  {
+    const uint32_t rr = load_row(rj);
+    const char* drow = dg + 2 * a.mdo.row_off(rr) + half * 16;
+    const char* orow = og + 2 * a.mo.row_off(rr) + half * 16;
+    float dsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const uint4 dr = *(const uint4*)(drow + kk * 32);
+      const uint4 orw = *(const uint4*)(orow + kk * 32);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf(elem<false>(&dr, e), elem<OF16>(&orw, e), dsum);
+    }
+    dsum = sum_halves(dsum);
+    if (half == 0) stat_d[rj] = rok ? dsum : 0.f;
+    else stat_l[rj] = rok ? a.lse[(size_t)p.u * L + rj] : 0.f;
+  }
+  // dS of the unit, rows of queries: [query block][query][key]
+  __shared__ __attribute__((aligned(16))) __bf16 dst[2 * BN * DS_PITCH];
+  __builtin_amdgcn_s_waitcnt(0);   // every direct load and LDS store is in place
+  __builtin_amdgcn_s_barrier();
+
+  const bool active = wave * 32 < L;
+  const char* kown = wave == 0 ? BStage<D, 0, 4>::ptr() : BStage<D, 1, 4>::ptr();
+  const char* vown = wave == 0 ? BStage<D, 0, 5>::ptr() : BStage<D, 1, 5>::ptr();
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dka[mt][r] = 0.f; dva[mt][r] = 0.f; }
+  const float c = a.c;
+  auto step = [&](uint32_t qb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    const char* qs = BStage<D, ST, 2>::ptr();
+    const char* ds = BStage<D, ST, 3>::ptr();
+    f32x16 sc, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      sc = mfma(read_rows<false>(qs, lay, kk), read_rows<false>(kown, lay, kk), sc);
+      dp = mfma(read_rows<false>(ds, lay, kk), read_rows<VF16>(vown, lay, kk), dp);
+    }
+    // queries past the end: weight 0
+    uint32_t qm = 0xffffffffu;
+    if ((qb + 1) * BN > L) qm = (1u << (L - qb * BN)) - 1u;
+    qm >>= 4 * half;
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      // queries 8 g + 4 half + (0..3) of the block
+      const float4 ls = *(const float4*)&stat_l[qb * BN + 8 * g + 4 * half];
+      const float4 dd = *(const float4*)&stat_d[qb * BN + 8 * g + 4 * half];
+      const float lv[4] = {ls.x, ls.y, ls.z, ls.w};
+      const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        const bool qin = __builtin_amdgcn_ubfe(qm, 8 * g + e, 1);
+        const float pij = qin ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e])) : 0.f;
+        pb[r / 8][r % 8] = (__bf16)pij;
+        sb[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dv4[e]));
+      }
+    }
+#pragma unroll
+    for (int jk = 0; jk < 2; ++jk)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        dva[mt] = mfma(read_tr<D, false>(ds, lay, jk, mt), pb[jk], dva[mt]);
+        dka[mt] = mfma(read_tr<D, false>(qs, lay, jk, mt), sb[jk], dka[mt]);
+      }
+    // dS rows for dq: keys past the end take no part
+    __bf16* drow = dst + qb * BN * DS_PITCH + rj;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      drow[(8 * (r / 4) + 4 * half + (r % 4)) * DS_PITCH] = rok ? sb[r / 8][r % 8] : (__bf16)0.f;
+  };
+  if (active) {
+    step(0, std::integral_constant<int, 0>{});
+    if (nb > 1) step(1, std::integral_constant<int, 1>{});
+    if (rok) {
+      const int64_t kbase = a.mdk.base(p.b, p.h, p.s) + a.mdk.row_off(rj);
+      store_rows<D>(dka, a.scale, half, a.final_pass, a.dk_acc + kbase,
+                    a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr);
+      const int64_t vbase = a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(rj);
+      store_rows<D>(dva, 1.f, half, kAccFinal, nullptr, (__bf16*)a.dv + vbase);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's dS rows are written
+  __builtin_amdgcn_s_barrier();
+  if (!active) return;
+
+  // dq^T of query block `wave` over the unit's keys: B = dS^T (this lane's query
+  // row, keys 16 jk + 4 half + (0..3) and 16 jk + 8 + 4 half + (0..3) of each key
+  // block: the row order of the transposing read of K)
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+  const __bf16* qrow = dst + wave * BN * DS_PITCH + l32 * DS_PITCH + 4 * half;
+  auto dq_block = [&](uint32_t kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    const char* ks = BStage<D, ST, 4>::ptr();
+#pragma unroll
+    for (int jk = 0; jk < 2; ++jk) {
+      const uint2 lo = *(const uint2*)(qrow + kb * BN + 16 * jk);
+      const uint2 hi = *(const uint2*)(qrow + kb * BN + 16 * jk + 8);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) acc[mt] = mfma(read_tr<D, false>(ks, lay, jk, mt), b, acc[mt]);
+    }
+  };
+  dq_block(0, std::integral_constant<int, 0>{});
+  if (nb > 1) dq_block(1, std::integral_constant<int, 1>{});
+  if (rok) {
+    const int64_t base = a.mdq.base(p.b, p.h, p.s) + a.mdq.row_off(rj);
+    store_rows<D>(acc, a.scale, half, a.final_pass, a.dq_acc + base,
+                  a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr);
+  }
+}
+
 template <int D, int NW, bool VF16, bool OF16, typename Args>
 hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8 * a.nchunks;
@@ -685,6 +868,35 @@ hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hip
 
 hipError_t launch_bwd_bf16_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream) {
   return launch_nw<true, true>(a, head_dim, kind_b, stream);
+}
+
+namespace {
+template <bool VF16, bool OF16, typename Args>
+hipError_t launch_small(Args a, int head_dim, hipStream_t stream) {
+  if (a.L > SMALL_ROWS || a.cut.on) return hipErrorInvalidValue;
+  a.nchunks = 1;
+  const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
+  if (head_dim == 128)
+    hipLaunchKernelGGL((bwd_small_bf16<128, VF16, OF16, Args>), dim3((uint32_t)blocks), dim3(128), 0, stream, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((bwd_small_bf16<64, VF16, OF16, Args>), dim3((uint32_t)blocks), dim3(128), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+}  // namespace
+
+bool bwd_bf16_fused(uint32_t L, bool cut) { return L <= SMALL_ROWS && !cut; }
+
+hipError_t launch_bwd_bf16_small(BwdArgs a, int head_dim, BwdTypes t, hipStream_t stream) {
+  if (t.v_f16 && !t.o_f16) return launch_small<true, false>(a, head_dim, stream);
+  if (!t.v_f16 && t.o_f16) return launch_small<false, true>(a, head_dim, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bf16_small_k(BwdArgsK a, int head_dim, hipStream_t stream) {
+  return launch_small<true, true>(a, head_dim, stream);
 }
 
 }  // namespace squad

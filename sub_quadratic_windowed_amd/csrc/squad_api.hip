@@ -394,6 +394,8 @@ int64_t kpass_rows(const KGeo& kg, int j) {
 
 int run_bwd(const BwdArgs& a, int32_t head_dim, int32_t dtype, BwdTypes t, hipStream_t s) {
   if (a.units == 0 || a.L == 0) return SQUAD_OK;
+  if (dtype == SQUAD_DTYPE_BF16 && bwd_bf16_fused(a.L, a.cut.on))
+    return launch_bwd_bf16_small(a, head_dim, t, s) == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
   for (int kind = 0; kind < 2; ++kind) {
     const hipError_t e = dtype == SQUAD_DTYPE_BF16 ? launch_bwd_bf16(a, head_dim, t, kind == 1, s)
                                                    : launch_bwd_f32(a, head_dim, kind == 1, s);
@@ -1030,7 +1032,9 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
       a.mqk = kpass_map(kg, j, heads, head_dim);
       fill(a);
       if (a.units == 0) continue;
-      for (int kind = 0; kind < 2 && !st; ++kind) {
+      if (bf16 && bwd_bf16_fused(a.L, false))
+        st = launch_bwd_bf16_small_k(a, head_dim, s) == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+      for (int kind = 0; kind < 2 && !st && !(bf16 && bwd_bf16_fused(a.L, false)); ++kind) {
         const hipError_t e = bf16 ? launch_bwd_bf16_k(a, head_dim, kind == 1, s)
                                   : launch_bwd_f32_k(a, head_dim, kind == 1, s);
         st = e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;

@@ -134,6 +134,11 @@ hipError_t launch_mfma_probe(float* out, int32_t blocks, int32_t iters, hipStrea
 hipError_t launch_bwd_bf16(BwdArgs a, int head_dim, BwdTypes t, bool kind_b, hipStream_t stream);
 // middle levels: fp16 values and outputs
 hipError_t launch_bwd_bf16_k(BwdArgsK a, int head_dim, bool kind_b, hipStream_t stream);
+// Units of at most 64 rows on a whole tiling: one kernel forms dq, dk and dv
+// (and D) in place of the two kinds.
+bool bwd_bf16_fused(uint32_t L, bool cut);
+hipError_t launch_bwd_bf16_small(BwdArgs a, int head_dim, BwdTypes t, hipStream_t stream);
+hipError_t launch_bwd_bf16_small_k(BwdArgsK a, int head_dim, hipStream_t stream);
 
 // Row-permutation copy: rows e = (bh * U + s) * L + r for bh < BH, s < U, r < L;
 // row e is read at src + ms(b, h, s, r) and written at dst + md(b, h, s, r).
