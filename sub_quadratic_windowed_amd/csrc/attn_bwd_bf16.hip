@@ -31,6 +31,10 @@
 // keeps two and requests the next block before using the current one.  Units of
 // at most 512 rows form their rows' byte offsets once, into LDS tables.
 //
+// Units of at most 64 rows (whole tilings) take one fused kernel instead: a
+// two-wave workgroup holds the whole unit, forms S and dP once (kind B's layout)
+// and passes dS through LDS to the dq product (see bwd_small_bf16).
+//
 // Products are bf16 with fp32 accumulation, except the global pass's dP^T: its
 // values are the fp16 local output, so it runs on fp16 MFMAs against dout scaled
 // per row by a power of two into fp16 range (undone on the fp32 result).  Elsewhere
@@ -636,20 +640,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // A whole unit of at most 64 rows in one two-wave workgroup: S and dP are formed
 // once and feed all three gradients (five products instead of the seven of kinds A
-// and B, and every row read once).  All of the unit's Q, dout, K and V rows sit in
-// LDS (grouped layout, two blocks each).  Wave w owns keys 32 w .. 32 w + 31 as in
-// kind B (S = Q K^T, dP = dout V^T with B = its key rows; dv^T += dout^T P,
-// dk^T += Q^T dS) and writes dS to LDS as rows of queries; once both waves' keys
-// are in, wave w forms dq^T of query block w as K^T dS^T (A = K^T by the
-// transposing read, B = dS^T rows in the key order of that read).  D = <dout, o>
-// of the unit's rows is formed in the prologue, one row per lane pair.
+// and B, and every row read once).  The unit's Q, dout and K rows sit in LDS
+// (grouped layout, two blocks each); wave w owns keys 32 w .. 32 w + 31 as in
+// kind B, with its V rows in registers (S = Q K^T, dP = dout V^T; dv^T += dout^T P,
+// dk^T += Q^T dS), and keeps its dS in registers.  Once every wave is done with
+// the dout blocks, the dS rows (queries) go to their place, and wave w forms dq^T
+// of query block w as K^T dS^T (A = K^T by the transposing read, B = dS^T rows in
+// the key order of that read).  D = <dout, o> of the unit's rows is formed in the
+// prologue.  LDS: 48 KB at head dim 128, so three workgroups share a CU.
 constexpr int SMALL_ROWS = 64;
-constexpr int DS_PITCH = 2 * BN + 8;   // 16-bit elements per dS row (8 of padding)
 
 template <int D, bool VF16, bool OF16, typename Args>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void bwd_small_bf16(Args a) {
   constexpr int NW = 2;
   typedef BCfg<D, NW> C;
+  // dS row pitch (16-bit elements): 64 keys, padded where the dout block has room
+  constexpr int PITCH = BN * D >= BN * (2 * BN + 8) ? 2 * BN + 8 : 2 * BN;
+  static_assert(BN * PITCH <= BN * D, "a block of dS rows fits a dout block");
   UnitPos p;
   if (!unit_pos(a, p)) return;   // one workgroup per unit (nchunks = 1)
   const uint32_t tid = threadIdx.x;
@@ -667,7 +674,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
 
   Layout<D, NW> lay;
   lay.init(lane, wave);
-  // every row of the unit: Q, dout, K and V blocks by direct loads (rows past the
+  // every row of the unit: Q, dout and K blocks by direct loads (rows past the
   // end read the last row; their scores are masked and their dS is zero)
   auto issue = [&](uint32_t b, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
@@ -682,20 +689,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(dg + 2 * a.mdo.row_off(r) + lay.ld_byte[i]),
                                        (lds_void_t*)(BStage<D, ST, 3>::ptr() + ins * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg + 2 * a.mv.row_off(r) + lay.ld_byte[i]),
-                                       (lds_void_t*)(BStage<D, ST, 5>::ptr() + ins * 1024), 16, 0, 0);
     }
   };
   issue(0, std::integral_constant<int, 0>{});
   if (nb > 1) issue(1, std::integral_constant<int, 1>{});
 
+  const uint32_t rj = wave * 32 + l32;   // this lane's key (dk, dv) and query (dq)
+  const bool rok = rj < L;
+  const uint32_t rr = load_row(rj);
+  // the own V rows (B operands of dP), bf16
+  bf16x8 vf[D / 16];
+  load_row_frags<D, VF16>(vg + 2 * a.mv.row_off(rr), half, vf);
   // row statistics of the unit: lse and D = <dout, o> (wave w: rows 32 w + l32)
   __shared__ __attribute__((aligned(16))) float stat_l[SMALL_ROWS];
   __shared__ __attribute__((aligned(16))) float stat_d[SMALL_ROWS];
-  const uint32_t rj = wave * 32 + l32;   // this lane's key (kind-B role) and query (dq)
-  const bool rok = rj < L;
   {
-    const uint32_t rr = load_row(rj);
     const char* drow = dg + 2 * a.mdo.row_off(rr) + half * 16;
     const char* orow = og + 2 * a.mo.row_off(rr) + half * 16;
     float dsum = 0.f;
@@ -710,19 +718,17 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     if (half == 0) stat_d[rj] = rok ? dsum : 0.f;
     else stat_l[rj] = rok ? a.lse[(size_t)p.u * L + rj] : 0.f;
   }
-  // dS of the unit, rows of queries: [query block][query][key]
-  __shared__ __attribute__((aligned(16))) __bf16 dst[2 * BN * DS_PITCH];
   __builtin_amdgcn_s_waitcnt(0);   // every direct load and LDS store is in place
   __builtin_amdgcn_s_barrier();
 
   const bool active = wave * 32 < L;
   const char* kown = wave == 0 ? BStage<D, 0, 4>::ptr() : BStage<D, 1, 4>::ptr();
-  const char* vown = wave == 0 ? BStage<D, 0, 5>::ptr() : BStage<D, 1, 5>::ptr();
   f32x16 dka[D / 32], dva[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dka[mt][r] = 0.f; dva[mt][r] = 0.f; }
+  bf16x8 sbk[2][2];   // dS of each query block (S layout: this lane's key)
   const float c = a.c;
   auto step = [&](uint32_t qb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
@@ -734,13 +740,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       sc = mfma(read_rows<false>(qs, lay, kk), read_rows<false>(kown, lay, kk), sc);
-      dp = mfma(read_rows<false>(ds, lay, kk), read_rows<VF16>(vown, lay, kk), dp);
+      dp = mfma(read_rows<false>(ds, lay, kk), vf[kk], dp);
     }
     // queries past the end: weight 0
     uint32_t qm = 0xffffffffu;
     if ((qb + 1) * BN > L) qm = (1u << (L - qb * BN)) - 1u;
     qm >>= 4 * half;
-    bf16x8 pb[2], sb[2];
+    bf16x8 pb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // queries 8 g + 4 half + (0..3) of the block
@@ -754,7 +760,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
         const bool qin = __builtin_amdgcn_ubfe(qm, 8 * g + e, 1);
         const float pij = qin ? __builtin_amdgcn_exp2f(fmaf(sc[r], c, -lv[e])) : 0.f;
         pb[r / 8][r % 8] = (__bf16)pij;
-        sb[r / 8][r % 8] = (__bf16)(pij * (dp[r] - dv4[e]));
+        sbk[ST][r / 8][r % 8] = (__bf16)(pij * (dp[r] - dv4[e]));
       }
     }
 #pragma unroll
@@ -762,13 +768,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
         dva[mt] = mfma(read_tr<D, false>(ds, lay, jk, mt), pb[jk], dva[mt]);
-        dka[mt] = mfma(read_tr<D, false>(qs, lay, jk, mt), sb[jk], dka[mt]);
+        dka[mt] = mfma(read_tr<D, false>(qs, lay, jk, mt), sbk[ST][jk], dka[mt]);
       }
-    // dS rows for dq: keys past the end take no part
-    __bf16* drow = dst + qb * BN * DS_PITCH + rj;
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      drow[(8 * (r / 4) + 4 * half + (r % 4)) * DS_PITCH] = rok ? sb[r / 8][r % 8] : (__bf16)0.f;
   };
   if (active) {
     step(0, std::integral_constant<int, 0>{});
@@ -779,6 +780,20 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
                     a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr);
       const int64_t vbase = a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(rj);
       store_rows<D>(dva, 1.f, half, kAccFinal, nullptr, (__bf16*)a.dv + vbase);
+    }
+  }
+  // every wave is done with the dout blocks: they take the dS rows of their query
+  // block ([query][key], PITCH apart); keys past the end take no part
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  __bf16* ds0 = (__bf16*)BStage<D, 0, 3>::ptr();
+  __bf16* ds1 = (__bf16*)BStage<D, 1, 3>::ptr();
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t q = 8 * (r / 4) + 4 * half + (r % 4);
+      ds0[q * PITCH + rj] = rok ? sbk[0][r / 8][r % 8] : (__bf16)0.f;
+      if (nb > 1) ds1[q * PITCH + rj] = rok ? sbk[1][r / 8][r % 8] : (__bf16)0.f;
     }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's dS rows are written
@@ -793,7 +808,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
-  const __bf16* qrow = dst + wave * BN * DS_PITCH + l32 * DS_PITCH + 4 * half;
+  const __bf16* qrow = (wave == 0 ? ds0 : ds1) + l32 * PITCH + 4 * half;
   auto dq_block = [&](uint32_t kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const char* ks = BStage<D, ST, 4>::ptr();
