@@ -66,6 +66,7 @@ BWD_CASES = [
     ((5, 12, 20), (2, 5, 6), 1, 2, 128, torch.bfloat16, False),
     ((4, 8, 8), (1, 8, 8), 1, 2, 128, torch.bfloat16, True),      # W = 64: two-wave workgroups
     ((5, 13, 4), (5, 13, 1), 1, 2, 128, torch.bfloat16, False),   # W = 65: four-wave, one row past
+    ((3, 11, 4), (3, 11, 1), 2, 2, 128, torch.bfloat16, True),    # W = 33: a second block of one row
     ((4, 8, 8), (1, 8, 8), 1, 2, 64, torch.float32, False),
 ]
 
