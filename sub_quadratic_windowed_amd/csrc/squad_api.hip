@@ -1032,12 +1032,14 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
       a.mqk = kpass_map(kg, j, heads, head_dim);
       fill(a);
       if (a.units == 0) continue;
-      if (bf16 && bwd_bf16_fused(a.L, false))
+      if (bf16 && bwd_bf16_fused(a.L, false)) {
         st = launch_bwd_bf16_small_k(a, head_dim, s) == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
-      for (int kind = 0; kind < 2 && !st && !(bf16 && bwd_bf16_fused(a.L, false)); ++kind) {
-        const hipError_t e = bf16 ? launch_bwd_bf16_k(a, head_dim, kind == 1, s)
-                                  : launch_bwd_f32_k(a, head_dim, kind == 1, s);
-        st = e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+      } else {
+        for (int kind = 0; kind < 2 && !st; ++kind) {
+          const hipError_t e = bf16 ? launch_bwd_bf16_k(a, head_dim, kind == 1, s)
+                                    : launch_bwd_f32_k(a, head_dim, kind == 1, s);
+          st = e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+        }
       }
     }
     if (st) return st;
