@@ -242,6 +242,58 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float sc
     }
 }
 
+// store_rows through LDS: the wave's 32 rows (lane l32 owns row l32, whose element
+// offset is `off`, negative for a row not to store) pass through `stage` (32 rows x
+// D / 2 fp32, 128 D bytes, the wave's own) half a row at a time, and go out as
+// whole row segments, 16 bytes per lane (64 / (D / 8) rows per store instruction)
+// instead of 16-byte pieces of 32 rows.  Chunks are XOR-swizzled by row in LDS.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], float scale, uint32_t lane,
+                                               uint32_t mode, float* accp, __bf16* outp, int32_t off,
+                                               char* stage) {
+  constexpr int DR = D / 2;        // fp32 dims per round
+  constexpr int NCH = DR / 4;      // 16-byte chunks per staged row
+  constexpr int MTR = D / 64;      // accumulator tiles per round
+  constexpr int RPI = 64 / NCH;    // rows per store instruction
+  const uint32_t half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+#pragma unroll
+    for (int m = 0; m < MTR; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int mt = rd * MTR + m;
+        const uint32_t ch = 8 * m + 2 * g + half;
+        *(float4*)(stage + l32 * (DR * 4) + ((ch ^ (l32 & (NCH - 1))) << 4)) =
+            make_float4(acc[mt][4 * g] * scale, acc[mt][4 * g + 1] * scale, acc[mt][4 * g + 2] * scale,
+                        acc[mt][4 * g + 3] * scale);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the staged half rows are in LDS
+    const uint32_t c = lane % NCH;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const uint32_t r = i * RPI + lane / NCH;
+      const int32_t o = __shfl(off, (int)r, 64);
+      float4 x = *(const float4*)(stage + r * (DR * 4) + ((c ^ (r & (NCH - 1))) << 4));
+      if (o >= 0) {
+        const int d0 = DR * rd + 4 * c;
+        if (mode != kAccWrite && accp) {
+          const float4 y = *(const float4*)(accp + o + d0);
+          x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+        }
+        if (mode == kAccFinal) {
+          bf16x4 w;
+          w[0] = (__bf16)x.x; w[1] = (__bf16)x.y; w[2] = (__bf16)x.z; w[3] = (__bf16)x.w;
+          *(bf16x4*)(outp + o + d0) = w;
+        } else {
+          *(float4*)(accp + o + d0) = x;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the stage is read before it is rewritten
+  }
+}
+
 // ---------------------------------------------------------------- kind A: dq (and D)
 
 template <int D, int NW, bool VF16, bool OF16, bool CUT, bool TAB, typename Args = BwdArgs>
@@ -774,20 +826,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   if (active) {
     step(0, std::integral_constant<int, 0>{});
     if (nb > 1) step(1, std::integral_constant<int, 1>{});
-    if (rok) {
-      const int64_t kbase = a.mdk.base(p.b, p.h, p.s) + a.mdk.row_off(rj);
-      store_rows<D>(dka, a.scale, half, a.final_pass, a.dk_acc + kbase,
-                    a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr);
-      const int64_t vbase = a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(rj);
-      store_rows<D>(dva, 1.f, half, kAccFinal, nullptr, (__bf16*)a.dv + vbase);
-    }
   }
-  // every wave is done with the dout blocks: they take the dS rows of their query
-  // block ([query][key], PITCH apart); keys past the end take no part
+  // every wave is done with the Q and dout blocks: the dout blocks take the dS rows
+  // of their query block ([query][key], PITCH apart; keys past the end take no
+  // part), and each wave stages its stores through its own Q block
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
   __bf16* ds0 = (__bf16*)BStage<D, 0, 3>::ptr();
   __bf16* ds1 = (__bf16*)BStage<D, 1, 3>::ptr();
+  char* own_stage = wave == 0 ? BStage<D, 0, 2>::ptr() : BStage<D, 1, 2>::ptr();
   if (active) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -795,6 +842,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
       ds0[q * PITCH + rj] = rok ? sbk[0][r / 8][r % 8] : (__bf16)0.f;
       if (nb > 1) ds1[q * PITCH + rj] = rok ? sbk[1][r / 8][r % 8] : (__bf16)0.f;
     }
+    const int64_t kb0 = a.mdk.base(p.b, p.h, p.s), vb0 = a.mdv.base(p.b, p.h, p.s);
+    store_rows_lds<D>(dka, a.scale, lane, a.final_pass, a.dk_acc + kb0,
+                      a.final_pass == kAccFinal ? (__bf16*)a.dk + kb0 : nullptr,
+                      rok ? (int32_t)a.mdk.row_off(rj) : -1, own_stage);
+    store_rows_lds<D>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vb0,
+                      rok ? (int32_t)a.mdv.row_off(rj) : -1, own_stage);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's dS rows are written
   __builtin_amdgcn_s_barrier();
@@ -823,11 +876,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   };
   dq_block(0, std::integral_constant<int, 0>{});
   if (nb > 1) dq_block(1, std::integral_constant<int, 1>{});
-  if (rok) {
-    const int64_t base = a.mdq.base(p.b, p.h, p.s) + a.mdq.row_off(rj);
-    store_rows<D>(acc, a.scale, half, a.final_pass, a.dq_acc + base,
-                  a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr);
-  }
+  const int64_t qb0 = a.mdq.base(p.b, p.h, p.s);
+  store_rows_lds<D>(acc, a.scale, lane, a.final_pass, a.dq_acc + qb0,
+                    a.final_pass == kAccFinal ? (__bf16*)a.dq + qb0 : nullptr,
+                    rok ? (int32_t)a.mdq.row_off(rj) : -1, own_stage);
 }
 
 template <int D, int NW, bool VF16, bool OF16, typename Args>
