@@ -216,37 +216,16 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Store a transposed accumulator tile set (element (dim 32 mt + 8 (r/4) + 4 half +
-// r % 4) of this lane's row) as fp32 (accumulate or plain) or bf16.
-template <int D>
-__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float scale, uint32_t half,
-                                           uint32_t mode, float* accp, __bf16* outp) {
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * mt + 8 * g + 4 * half;
-      float4 x = make_float4(acc[mt][4 * g] * scale, acc[mt][4 * g + 1] * scale, acc[mt][4 * g + 2] * scale,
-                             acc[mt][4 * g + 3] * scale);
-      if (mode != kAccWrite && accp) {
-        const float4 y = *(const float4*)(accp + d0);
-        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
-      }
-      if (mode == kAccFinal) {
-        bf16x4 w;
-        w[0] = (__bf16)x.x; w[1] = (__bf16)x.y; w[2] = (__bf16)x.z; w[3] = (__bf16)x.w;
-        *(bf16x4*)(outp + d0) = w;
-      } else {
-        *(float4*)(accp + d0) = x;
-      }
-    }
-}
-
-// store_rows through LDS: the wave's 32 rows (lane l32 owns row l32, whose element
-// offset is `off`, negative for a row not to store) pass through `stage` (32 rows x
-// D / 2 fp32, 128 D bytes, the wave's own) half a row at a time, and go out as
-// whole row segments, 16 bytes per lane (64 / (D / 8) rows per store instruction)
-// instead of 16-byte pieces of 32 rows.  Chunks are XOR-swizzled by row in LDS.
+// Store a transposed accumulator tile set: lane l32 (and l32 + 32) owns row l32,
+// holding its element dim 32 mt + 8 (r / 4) + 4 half + r % 4 in acc[mt][r]; `off` is
+// the row's element offset (negative: not stored).  Each value is scaled, then
+// written as fp32 (kAccWrite), added to the fp32 accumulator and written back
+// (kAccAdd), or added to it and written as bf16 to outp (kAccFinal; with no
+// accumulator, plainly written).  The rows pass through `stage` (32 rows x D / 2
+// fp32 = 64 D bytes of LDS, the wave's own) half a row at a time and go out as
+// whole row segments, 16 bytes per lane, so a store instruction covers 64 / (D / 8)
+// rows' contiguous bytes rather than 16-byte pieces of 32 rows.  Chunks are
+// XOR-swizzled by row in LDS.
 template <int D>
 __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], float scale, uint32_t lane,
                                                uint32_t mode, float* accp, __bf16* outp, int32_t off,
@@ -491,10 +470,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (kb < nkb) step(kb, std::integral_constant<int, 0>{}, std::false_type{});
   if (kb + 1 < nkb) step(kb + 1, std::integral_constant<int, 1>{}, std::false_type{});
 
-  if (active && qok) {
-    const int64_t base = a.mdq.base(p.b, p.h, p.s) + a.mdq.row_off(qi);
-    store_rows<D>(acc, a.scale, half, a.final_pass, a.dq_acc + base,
-                  a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr);
+  // (every wave is past the last step's barrier: the stages are free, and wave w
+  // stages its stores in one of them)
+  if (active) {
+    char* st = wave == 0 ? BStage<D, 0, 0>::ptr()
+             : wave == 1 ? BStage<D, 1, 0>::ptr()
+             : wave == 2 ? BStage<D, 2, 0>::ptr() : BStage<D, 0, 1>::ptr();
+    const int64_t base = a.mdq.base(p.b, p.h, p.s);
+    store_rows_lds<D>(acc, a.scale, lane, a.final_pass, a.dq_acc + base,
+                      a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr,
+                      qok ? (int32_t)a.mdq.row_off(qi) : -1, st);
   }
 }
 
@@ -679,12 +664,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (qb < nqb) step(qb, std::integral_constant<int, 0>{}, std::false_type{});
   if (qb + 1 < nqb) step(qb + 1, std::integral_constant<int, 1>{}, std::false_type{});
 
-  if (active && kok) {
-    const int64_t kbase = a.mdk.base(p.b, p.h, p.s) + a.mdk.row_off(kj);
-    store_rows<D>(dka, a.scale, half, a.final_pass, a.dk_acc + kbase,
-                  a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr);
-    const int64_t vbase = a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(kj);
-    store_rows<D>(dva, 1.f, half, kAccFinal, nullptr, (__bf16*)a.dv + vbase);
+  // (every wave is past the last step's barrier: wave w stages its stores in its
+  // own 32 rows of the V block)
+  if (active) {
+    char* st = (char*)vown + wave * 32 * D * 2;
+    const int64_t kbase = a.mdk.base(p.b, p.h, p.s), vbase = a.mdv.base(p.b, p.h, p.s);
+    store_rows_lds<D>(dka, a.scale, lane, a.final_pass, a.dk_acc + kbase,
+                      a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr,
+                      kok ? (int32_t)a.mdk.row_off(kj) : -1, st);
+    store_rows_lds<D>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vbase,
+                      kok ? (int32_t)a.mdv.row_off(kj) : -1, st);
   }
 }
 
