@@ -416,8 +416,8 @@ def squad_forward_stats(q, k, grid, tile, scale=None):
 
 
 # ---- more than two passes (the pages name composing more than two passes as
-# future work, to trade depth for efficiency; technical summary, "Beperkingen en
-# Conclusie") ----
+# future work, to trade depth for efficiency; technical summary, "Betekenis en
+# Claims") ----
 
 def _kpass_levels(grid, tiles):
     """Per-axis level sizes of a nested tiling: tiles[0] | tiles[1] | ... | grid."""

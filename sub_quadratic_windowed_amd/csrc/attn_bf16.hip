@@ -170,11 +170,22 @@ struct Stage {
   }
 };
 
+// The 16 score-register bits of lane half h for one 32-row block whose presence
+// word has bit j set when row j is present: register r holds row 8*(r/4) + 4*h + r%4
+// (the MFMA output layout), i.e. the nibbles at 4*h, 8 + 4*h, 16 + 4*h, 24 + 4*h.
+__device__ __forceinline__ uint32_t half_bits(uint32_t rows, uint32_t h) {
+  uint32_t x = (rows >> (4 * h)) & 0x0f0f0f0fu;
+  x = (x | (x >> 4)) & 0x00ff00ffu;
+  x = (x | (x >> 8)) & 0x0000ffffu;
+  return x;
+}
+
 // CUT: the grid is not a whole number of tiles; absent rows (the far edges' cut
-// tiles) are neither keys nor stored queries (row tables only, TAB).
+// tiles) are neither keys nor stored queries.  With the row tables (TAB) their
+// presence bits are formed once per workgroup into LDS; without them, for each key
+// block one step ahead, with one ballot.
 template <int D, int NW, typename VT, typename OT, bool TAB, bool CUT = false, typename Args = AttnArgs>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(Args a) {
-  static_assert(TAB || !CUT, "cut tilings use the row tables");
   typedef Cfg<D, NW> C;
   typedef typename Vec<VT>::x8 vx8;
   typedef typename Vec<VT>::x4 vx4;
@@ -227,14 +238,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
   }
   // units of at most TABLE_ROWS rows: every row's offset is formed once, into LDS
-  __shared__ int32_t ktab[TAB ? TABLE_ROWS : 1];
-  __shared__ int32_t vtab[TAB ? TABLE_ROWS : 1];
+  __shared__ uint32_t ktab[TAB ? TABLE_ROWS : 1];
+  __shared__ uint32_t vtab[TAB ? TABLE_ROWS : 1];
   // cut tilings: which rows are present, per 32-row key block and per lane half.
   // A lane of half h holds score registers r = 0..15 for the block's rows
   // 8*(r/4) + 4*h + r%4 (the MFMA output layout); entry 2*kb + h has bit r set
   // when that row is present, so the score mask tests constant bit positions.
-  __shared__ uint32_t rmask[CUT ? TABLE_ROWS / 16 : 1];
-  if constexpr (CUT) {
+  __shared__ uint32_t rmask[CUT && TAB ? TABLE_ROWS / 16 : 1];
+  if constexpr (CUT && TAB) {
     // byte offsets; absent rows (and rows past the end, up to a whole block) read row 0
     const uint32_t iters = (nkb * BN + C::NT - 1) / C::NT;
     for (uint32_t i = 0; i < iters; ++i) {
@@ -243,28 +254,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       const uint32_t rr = ok ? r : 0;
       const int32_t ko = a.mqk.row_off(rr);
       if (r < nkb * BN) {
-        ktab[r] = 2 * ko;
-        vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
+        ktab[r] = bytes16(ko);
+        vtab[r] = bytes16(a.v_like_k ? ko : a.mv.row_off(rr));
       }
       const uint64_t bits = __ballot(ok);
       // this wave's 64 rows are key blocks w0 and w0 + 1; lanes 0..3 each compact
       // one (block, half) pair: the nibbles at 4*h, 8 + 4*h, 16 + 4*h, 24 + 4*h
       const uint32_t w0 = (i * C::NT + 64 * wave) / 32;
-      if (lane < 4 && w0 + (lane >> 1) < TABLE_ROWS / 32) {
-        uint32_t x = (uint32_t)(bits >> (32 * (lane >> 1)));
-        x = (x >> (4 * (lane & 1))) & 0x0f0f0f0fu;
-        x = (x | (x >> 4)) & 0x00ff00ffu;
-        x = (x | (x >> 8)) & 0x0000ffffu;
-        rmask[2 * w0 + lane] = x;
-      }
+      if (lane < 4 && w0 + (lane >> 1) < TABLE_ROWS / 32)
+        rmask[2 * w0 + lane] = half_bits((uint32_t)(bits >> (32 * (lane >> 1))), lane & 1);
     }
   } else if constexpr (TAB) {
     // byte offsets; rows past the end of the unit (up to a whole block) repeat its last row
     for (uint32_t r = tid; r < nkb * BN; r += C::NT) {
       const uint32_t rr = min(r, L - 1);
       const int32_t ko = a.mqk.row_off(rr);
-      ktab[r] = 2 * ko;
-      vtab[r] = 2 * (a.v_like_k ? ko : a.mv.row_off(rr));
+      ktab[r] = bytes16(ko);
+      vtab[r] = bytes16(a.v_like_k ? ko : a.mv.row_off(rr));
     }
   }
   if constexpr (TAB) {
@@ -274,14 +280,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     __builtin_amdgcn_s_barrier();
   }
 
-  // lane l (< 32) locates key l of a block; lanes 32-63 mirror lanes 0-31
-  auto key_offset = [&](const auto& m, uint32_t kb) -> int32_t {
-    return m.row_off(min(kb * BN + l32, L - 1));
-  };
   const bool v_like_k = a.v_like_k != 0;
-  auto v_offset = [&](uint32_t kb, int32_t ko) -> int32_t {
-    return v_like_k ? ko : key_offset(a.mv, kb);
-  };
+  // cut tilings without the tables: this half's presence bits of the block in
+  // each stage (formed when the block's loads are prepared)
+  uint32_t kmask[3] = {0xffffu, 0xffffu, 0xffffu};
 
   // K: this wave's share of the block's direct loads.  Load `ins` fills rows
   // KRPI * ins ...; lane i carries row KRPI * ins + i / CPR, stored slot i % CPR,
@@ -307,27 +309,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // Loads of one block are prepared (row offsets located, lanes' 32-bit element
   // offsets formed) one step before they are issued, so the shuffles and the
   // address arithmetic stay off the path between a block's barrier and its MFMAs.
-  int32_t pk[C::VPW], pv[C::VPW];
-  auto prep_block = [&](uint32_t kb) {
+  uint32_t pk[C::VPW], pv[C::VPW];
+  auto prep_block = [&](uint32_t kb, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
     if constexpr (TAB) {
 #pragma unroll
       for (int i = 0; i < C::VPW; ++i) {
         const int ins = wave + i * NW;
         const uint32_t krow = C::KRPI * ins + krow0;
         const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
-        pk[i] = ktab[kb * BN + (krow & 31)] + (int32_t)(kchunk * 16);
-        pv[i] = vtab[kb * BN + ((4 * C::GPI * ins + vrow0) & 31)] + (int32_t)(vcol * 16);
+        pk[i] = ktab[kb * BN + (krow & 31)] + kchunk * 16;
+        pv[i] = vtab[kb * BN + ((4 * C::GPI * ins + vrow0) & 31)] + vcol * 16;
       }
     } else {
-      const int32_t ko = key_offset(a.mqk, kb);
-      const int32_t vo = v_offset(kb, ko);
+      // lane l (< 32) locates key l of the block; lanes 32-63 mirror lanes 0-31.
+      // Rows past the end read the last row; on cut tilings absent rows read row 0
+      uint32_t r = kb * BN + l32;
+      if constexpr (CUT) {
+        const bool ok = present(r);
+        kmask[ST] = half_bits((uint32_t)__ballot(ok), half);
+        r = ok ? r : 0;
+      } else {
+        r = min(r, L - 1);
+      }
+      const int32_t ko = a.mqk.row_off(r);
+      const int32_t vo = v_like_k ? ko : a.mv.row_off(r);
 #pragma unroll
       for (int i = 0; i < C::VPW; ++i) {
         const int ins = wave + i * NW;
         const uint32_t krow = C::KRPI * ins + krow0;
         const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
-        pk[i] = 2 * (shfl(ko, krow & 31) + (int32_t)(kchunk * 8));
-        pv[i] = 2 * (shfl(vo, (4 * C::GPI * ins + vrow0) & 31) + (int32_t)(vcol * 8));
+        pk[i] = bytes16(shfl(ko, krow & 31)) + kchunk * 16;
+        pv[i] = bytes16(shfl(vo, (4 * C::GPI * ins + vrow0) & 31)) + vcol * 16;
       }
     }
   };
@@ -341,21 +354,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       const int ins = wave + i * NW;
       if (C::VPW * NW != C::VINS && ins >= C::VINS) break;
       // uniform base + unsigned 32-bit byte offset: one offset register per load
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)kg + (uint32_t)pk[i]),
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)kg + pk[i]),
                                        (lds_void_t*)(ks + ins * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)vg + (uint32_t)pv[i]),
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)vg + pv[i]),
                                        (lds_void_t*)(vs + ins * 512), 16, 0, 0);
     }
   };
 
   // blocks 0 and 1 requested
-  prep_block(0);
+  prep_block(0, std::integral_constant<int, 0>{});
   issue_block(std::integral_constant<int, 0>{});
   if (nkb > 1) {
-    prep_block(1);
+    prep_block(1, std::integral_constant<int, 1>{});
     issue_block(std::integral_constant<int, 1>{});
   }
-  if (nkb > 2) prep_block(2);
+  if (nkb > 2) prep_block(2, std::integral_constant<int, 2>{});
   wait_vmcnt<0>();   // the query rows and blocks 0 and 1 have landed
   __builtin_amdgcn_s_barrier();
 
@@ -412,7 +425,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       if (ST == 0 && has2) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
       // keys past the end of the unit take no weight
       if constexpr (CUT) {
-        const uint32_t km = rmask[2 * kb + half];
+        uint32_t km;
+        if constexpr (TAB) km = rmask[2 * kb + half];
+        else km = kmask[ST];
         if (km != 0xffffu) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
@@ -468,7 +483,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       }
     }
     if (ST == 0 && has2 && !active) issue_block(std::integral_constant<int, (ST + 2) % 3>{});
-    if (ALL || kb + 3 < nkb) prep_block(kb + 3);
+    if (ALL || kb + 3 < nkb) prep_block(kb + 3, st_tag);
     // this wave's loads of block kb + 1 have landed (only block kb + 2 may be in
     // flight); the barrier then publishes them and retires stage ST's readers
     wait_loads(has2);
@@ -517,10 +532,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
     const uint32_t wcol = lane % C::CPR;
     const uint32_t wrow = lane / C::CPR;
     bool qok = q0 + l32 < L;
-    if constexpr (CUT) {
+    if constexpr (CUT && TAB) {
       // row x of block x / 32 sits in half (x / 4) % 2 at register 4 * ((x % 32) / 8) + x % 4
       const uint32_t x = q0 + l32;
       qok = qok && ((rmask[2 * (x >> 5) + ((x >> 2) & 1)] >> (4 * ((x & 31) >> 3) + (x & 3))) & 1);
+    } else if constexpr (CUT) {
+      qok = qok && present(q0 + l32);
     }
     if (a.lse && qok && half == 0) a.lse[(size_t)u * L + q0 + l32] = m_ref + __log2f(lsum);
     const int32_t oo = qok ? a.mo.row_off(q0 + l32) : -1;
@@ -541,10 +558,12 @@ hipError_t launch(const Args& a, hipStream_t stream) {
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   if constexpr (std::is_same<Args, AttnArgs>::value) {
     if (a.cut.on) {
-      // (the host allows cut tilings only where both passes use the row tables)
-      if (a.L > TABLE_ROWS) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0,
-                         stream, a);
+      if (a.L <= TABLE_ROWS)
+        hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, false, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0,
+                           stream, a);
       return hipGetLastError();
     }
   } else if (a.cut.on) {

@@ -122,8 +122,8 @@ struct BStage {
 constexpr int BT_ROWS = 512;
 template <bool TAB>
 struct RowTab {
-  static __device__ __forceinline__ int32_t* ptr() {
-    __shared__ int32_t t[TAB ? 2 * BT_ROWS : 1];
+  static __device__ __forceinline__ uint32_t* ptr() {
+    __shared__ uint32_t t[TAB ? 2 * BT_ROWS : 1];
     return t;
   }
 };
@@ -311,11 +311,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // query and upstream-gradient fragments; D = <dout, o> over this lane's dims
   bf16x8 qf[D / 16], df[D / 16];
-  load_row_frags<D, false>(qg + 2 * a.mqk.row_off(qr), half, qf);
-  load_row_frags<D, false>(dg + 2 * a.mdo.row_off(qr), half, df);
+  load_row_frags<D, false>(qg + bytes16(a.mqk.row_off(qr)), half, qf);
+  load_row_frags<D, false>(dg + bytes16(a.mdo.row_off(qr)), half, df);
   float dsum = 0.f;
   {
-    const char* orow = og + 2 * a.mo.row_off(qr) + half * 16;
+    const char* orow = og + bytes16(a.mo.row_off(qr)) + half * 16;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const uint4 raw = *(const uint4*)(orow + kk * 32);
@@ -353,12 +353,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   Layout<D, NW> lay;
   lay.init(lane, wave);
   const uint32_t nkb = (L + BN - 1) / BN;
-  int32_t* tab = RowTab<TAB>::ptr();   // K rows, then V rows (byte offsets)
+  uint32_t* tab = RowTab<TAB>::ptr();   // K rows, then V rows (byte offsets)
   if constexpr (TAB) {
     for (uint32_t r = tid; r < nkb * BN; r += 64 * NW) {
       const uint32_t rr = load_row(r);
-      tab[r] = 2 * a.mqk.row_off(rr);
-      tab[BT_ROWS + r] = 2 * a.mv.row_off(rr);
+      tab[r] = bytes16(a.mqk.row_off(rr));
+      tab[BT_ROWS + r] = bytes16(a.mv.row_off(rr));
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the table is written
     __builtin_amdgcn_s_barrier();
@@ -370,18 +370,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
-      int32_t ko, vo;
+      uint32_t ko, vo;
       if constexpr (TAB) {
         ko = tab[kb * BN + lay.ld_row[i]];
         vo = tab[BT_ROWS + kb * BN + lay.ld_row[i]];
       } else {
         const uint32_t r = load_row(kb * BN + lay.ld_row[i]);
-        ko = 2 * a.mqk.row_off(r);
-        vo = 2 * a.mv.row_off(r);
+        ko = bytes16(a.mqk.row_off(r));
+        vo = bytes16(a.mv.row_off(r));
       }
-      __builtin_amdgcn_global_load_lds((const void*)(kg + (uint32_t)ko + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(kg + ko + lay.ld_byte[i]),
                                        (lds_void_t*)(ks + ins * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg + (uint32_t)vo + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(vg + vo + lay.ld_byte[i]),
                                        (lds_void_t*)(vs + ins * 1024), 16, 0, 0);
     }
   };
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bool kok = present(kj);
   const uint32_t kr = load_row(kj);
   bf16x8 kf[D / 16];
-  load_row_frags<D, false>(kg + 2 * a.mqk.row_off(kr), half, kf);
+  load_row_frags<D, false>(kg + bytes16(a.mqk.row_off(kr)), half, kf);
   // the workgroup's own V rows, bf16, in LDS: chunk c of row r at slot c ^ (r % CPR)
   // (read as the B operand of dP, one 16-byte chunk per lane, conflict-free);
   // holding them in registers instead would not leave room for both accumulators
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const uint32_t ch = tid + 64 * NW * i;
       const uint32_t r = ch / C::CPR, cc = ch % C::CPR;
       const uint32_t vr = load_row(p.chunk * BM + r);
-      const uint4 raw = *(const uint4*)(vg + 2 * a.mv.row_off(vr) + 16 * cc);
+      const uint4 raw = *(const uint4*)(vg + bytes16(a.mv.row_off(vr)) + 16 * cc);
       *(bf16x8*)((char*)vown + r * D * 2 + ((cc ^ (r & (C::CPR - 1))) << 4)) = frag<VF16>(raw);
     }
   }
@@ -540,12 +540,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   lay.init(lane, wave);
   const size_t unit_rows = (size_t)p.u * L;
   const uint32_t nqb = (L + BN - 1) / BN;
-  int32_t* tab = RowTab<TAB>::ptr();   // Q rows, then dout rows (byte offsets)
+  uint32_t* tab = RowTab<TAB>::ptr();   // Q rows, then dout rows (byte offsets)
   if constexpr (TAB) {
     for (uint32_t r = tid; r < nqb * BN; r += 64 * NW) {
       const uint32_t rr = load_row(r);
-      tab[r] = 2 * a.mqk.row_off(rr);
-      tab[BT_ROWS + r] = 2 * a.mdo.row_off(rr);
+      tab[r] = bytes16(a.mqk.row_off(rr));
+      tab[BT_ROWS + r] = bytes16(a.mdo.row_off(rr));
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the table is written
     __builtin_amdgcn_s_barrier();
@@ -557,18 +557,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
-      int32_t qo, dof;
+      uint32_t qo, dof;
       if constexpr (TAB) {
         qo = tab[qb * BN + lay.ld_row[i]];
         dof = tab[BT_ROWS + qb * BN + lay.ld_row[i]];
       } else {
         const uint32_t r = load_row(qb * BN + lay.ld_row[i]);
-        qo = 2 * a.mqk.row_off(r);
-        dof = 2 * a.mdo.row_off(r);
+        qo = bytes16(a.mqk.row_off(r));
+        dof = bytes16(a.mdo.row_off(r));
       }
-      __builtin_amdgcn_global_load_lds((const void*)(qg + (uint32_t)qo + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(qg + qo + lay.ld_byte[i]),
                                        (lds_void_t*)(qs + ins * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(dg + (uint32_t)dof + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(dg + dof + lay.ld_byte[i]),
                                        (lds_void_t*)(ds + ins * 1024), 16, 0, 0);
     }
     // the block's row statistics by one more direct load (lane i < 32: lse of row
@@ -723,12 +723,12 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
       const uint32_t r = load_row(b * BN + lay.ld_row[i]);
-      const uint32_t qo = 2 * a.mqk.row_off(r) + lay.ld_byte[i];
+      const uint32_t qo = bytes16(a.mqk.row_off(r)) + lay.ld_byte[i];
       __builtin_amdgcn_global_load_lds((const void*)(qg + qo), (lds_void_t*)(BStage<D, ST, 2>::ptr() + ins * 1024),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(kg + qo), (lds_void_t*)(BStage<D, ST, 4>::ptr() + ins * 1024),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(dg + 2 * a.mdo.row_off(r) + lay.ld_byte[i]),
+      __builtin_amdgcn_global_load_lds((const void*)(dg + bytes16(a.mdo.row_off(r)) + lay.ld_byte[i]),
                                        (lds_void_t*)(BStage<D, ST, 3>::ptr() + ins * 1024), 16, 0, 0);
     }
   };
@@ -740,13 +740,13 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   const uint32_t rr = load_row(rj);
   // the own V rows (B operands of dP), bf16
   bf16x8 vf[D / 16];
-  load_row_frags<D, VF16>(vg + 2 * a.mv.row_off(rr), half, vf);
+  load_row_frags<D, VF16>(vg + bytes16(a.mv.row_off(rr)), half, vf);
   // row statistics of the unit: lse and D = <dout, o> (wave w: rows 32 w + l32)
   __shared__ __attribute__((aligned(16))) float stat_l[SMALL_ROWS];
   __shared__ __attribute__((aligned(16))) float stat_d[SMALL_ROWS];
   {
-    const char* drow = dg + 2 * a.mdo.row_off(rr) + half * 16;
-    const char* orow = og + 2 * a.mo.row_off(rr) + half * 16;
+    const char* drow = dg + bytes16(a.mdo.row_off(rr)) + half * 16;
+    const char* orow = og + bytes16(a.mo.row_off(rr)) + half * 16;
     float dsum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -877,11 +877,16 @@ hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
   if constexpr (std::is_same<Args, BwdArgs>::value) {
-    // (the host allows cut tilings only where the units fit the row tables)
+    // cut tilings: presence is tested per block (one ballot), with or without the tables
     if (a.cut.on) {
-      if (a.L > BT_ROWS) return hipErrorInvalidValue;
-      if (kind_b) hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, true, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, true, true>), grid, block, 0, stream, a);
+      const bool tab = a.L <= BT_ROWS;
+      if (kind_b) {
+        if (tab) hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, true, false>), grid, block, 0, stream, a);
+      } else {
+        if (tab) hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, true, false>), grid, block, 0, stream, a);
+      }
       return hipGetLastError();
     }
   } else if (a.cut.on) {

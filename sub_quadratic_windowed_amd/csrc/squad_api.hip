@@ -162,8 +162,6 @@ int check_grid_call(const int32_t grid[3], const int32_t tile[3], int32_t heads,
   if (too_many_units(bh, (uint64_t)(g.G > g.Wn ? g.G : g.Wn), bh * cells)) return SQUAD_ERR_SHAPE;
   // the kernels address rows inside one batch element with 32-bit offsets
   if (cells * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
-  // cut tilings mark absent rows in the per-unit row tables of the 16-bit engine
-  if (g.cut && dtype == SQUAD_DTYPE_BF16 && (g.G > 512 || g.Wn > 512)) return SQUAD_ERR_UNSUPPORTED;
   bytes = (size_t)bh * (size_t)g.n * (size_t)head_dim * elem_bytes(dtype);
   if (wbytes) *wbytes = (size_t)bh * (size_t)cells * (size_t)head_dim * elem_bytes(dtype);
   return SQUAD_OK;

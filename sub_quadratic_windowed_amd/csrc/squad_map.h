@@ -120,6 +120,12 @@ struct Mix32 {
   }
 };
 
+// Byte offset of a 16-bit element at element offset e (0 <= e < 2^31) inside one
+// (batch, head).  Formed in unsigned 32-bit arithmetic: exact up to 2^32 - 2 bytes
+// and zero-extended where it is added to a pointer (doubling a signed offset would
+// turn offsets of 2^30 elements and more negative).
+__host__ __device__ __forceinline__ uint32_t bytes16(int32_t e) { return 2u * (uint32_t)e; }
+
 struct RowMap {
   int64_t sB, sH; // batch and head strides (elements)
   Mix unit;       // unit index -> offset

@@ -68,6 +68,8 @@ BWD_CASES = [
     ((5, 13, 4), (5, 13, 1), 1, 2, 128, torch.bfloat16, False),   # W = 65: four-wave, one row past
     ((3, 11, 4), (3, 11, 1), 2, 2, 128, torch.bfloat16, True),    # W = 33: a second block of one row
     ((4, 8, 8), (1, 8, 8), 1, 2, 64, torch.float32, False),
+    ((5, 13, 20), (4, 12, 12), 1, 2, 128, torch.bfloat16, True),  # cut, Wn = 576 (past the row tables)
+    ((9, 31, 40), (2, 2, 2), 1, 2, 128, torch.bfloat16, False),   # cut, G = 1600 (past the row tables)
 ]
 
 

@@ -365,6 +365,8 @@ CUT_CASES = [
     ((8, 15, 15), (1, 2, 2), 1, 2, 128, torch.bfloat16, False),   # G = 512 groups of 1..4 present rows
     ((9, 32, 32), (2, 1, 1), 1, 1, 64, torch.float32, False),     # fp32: G = 5120 rows per group
     ((21, 45, 79), (3, 9, 10), 1, 2, 128, torch.bfloat16, False), # n = 74655, Wn = 270, G = 280, cut along w
+    ((5, 13, 20), (4, 12, 12), 1, 2, 128, torch.bfloat16, True),  # Wn = 576: local units past the row tables
+    ((9, 31, 40), (2, 2, 2), 1, 2, 128, torch.bfloat16, False),   # G = 1600: global units past the row tables
 ]
 
 
