@@ -46,13 +46,26 @@ def parse():
     p.add_argument("--no-permutations", action="store_true")
     p.add_argument("--no-tilings", action="store_true")
     p.add_argument("--no-backward", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=8, help="heads in the oracle's timed sample")
+    p.add_argument("--cpu-heads", type=int, default=0,
+                   help="heads in the oracle's timed run (default: all of the workload's heads)")
     return p.parse_args()
 
 
-def kernel_source_digest():
+# the sources each kernel family is built from (its kernel file, the shared maps and
+# launch interface, and the host code that sets up its arguments)
+KERNEL_SOURCES = {
+    "forward": ("attn_bf16.hip",),
+    "backward": ("attn_bwd_bf16.hip",),
+    "permute": ("permute.hip",),
+}
+SHARED_SOURCES = ("squad_map.h", "squad_kernels.h", "squad_api.hip")
+
+
+def kernel_source_digest(family="forward"):
+    """Digest of the sources of one kernel family: counters taken on other sources
+    do not describe the kernels that run."""
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "squad_map.h", "squad_kernels.h", "squad_api.hip"):
+    for f in KERNEL_SOURCES[family] + SHARED_SOURCES:
         with open(os.path.join(ROOT, "sub_quadratic_windowed_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -127,46 +140,66 @@ def mfma_probe(sq, stream, dev):
             "kernel": "4 independent 32x32x16 bf16 MFMA chains per wave, hash-drawn operands, 8192 waves"}
 
 
-def cpu_baseline(cfg, qc, kc, vc, heads):
-    """The float64 oracle as it stands, on `heads` of the workload's heads."""
-    import numpy as np
+def cpu_baseline(cfg, qc, kc, vc, heads, chunk=8):
+    """The float64 oracle as it stands, timed over `heads` of the workload's heads
+    (all of them by default).  Heads are independent, so it runs `chunk` heads per
+    call to bound its memory (at the high-resolution size one call over 8 heads
+    holds about 25 GB); the time is the sum over the calls."""
     import threadpoolctl
 
     import oracle
 
-    hs = list(range(heads))
-    q = qc[:, :, hs].double().numpy()
-    k = kc[:, :, hs].double().numpy()
-    v = vc[:, :, hs].double().numpy()
+    heads = heads or cfg.heads
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
-    t0 = time.perf_counter()
-    oracle.squad_forward(q, k, v, cfg.grid, cfg.tile)
-    dt = time.perf_counter() - t0
-    # tokens/s of the whole workload: the sample did heads/H of every token's work
+    dt = 0.0
+    calls = 0
+    for h0 in range(0, heads, chunk):
+        hs = list(range(h0, min(h0 + chunk, heads)))
+        q = qc[:, :, hs].double().numpy()
+        k = kc[:, :, hs].double().numpy()
+        v = vc[:, :, hs].double().numpy()
+        t0 = time.perf_counter()
+        oracle.squad_forward(q, k, v, cfg.grid, cfg.tile)
+        dt += time.perf_counter() - t0
+        calls += 1
+        del q, k, v
+    # tokens/s of the whole workload (scaled only if fewer than all heads ran)
     value = cfg.batch * cfg.n * (heads / cfg.heads) / dt
+    scaled = "" if heads == cfg.heads else f", scaled by {cfg.heads}/{heads} to the whole workload"
     return {
         "value": value,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"float64 numpy oracle, full forward over {heads} of {cfg.heads} heads "
-                  f"({cfg.batch}x{cfg.n} tokens, head_dim {cfg.head_dim}); {dt:.1f} s, scaled by "
-                  f"{cfg.heads}/{heads} to the whole workload",
+                  f"({cfg.batch}x{cfg.n} tokens, head_dim {cfg.head_dim}) in {calls} calls of up to "
+                  f"{chunk} heads; {dt:.1f} s{scaled}",
         "seconds": dt,
+        "blas_threads": threads,
+        "affinity_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": cpu_model(),
     }
 
 
 def cpu_model():
-    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    """The host CPU as /proc/cpuinfo names it: model name, family, model and
+    stepping numbers, and the logical CPU count; or None."""
+    fields, count = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key == "processor":
+                    count += 1
+                elif key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                    fields[key] = val.strip()
     except OSError:
-        pass
-    return None
+        return None
+    if "model name" not in fields:
+        return None
+    return (f"{fields['model name']} (family {fields.get('cpu family', '?')}, model {fields.get('model', '?')}, "
+            f"stepping {fields.get('stepping', '?')}), {count} logical CPUs")
 
 
 def main():
@@ -292,7 +325,7 @@ def main():
 
     base = None
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
+        print(f"[bench] cpu oracle on {args.cpu_heads or cfg.heads} heads", file=sys.stderr, flush=True)
         base = cpu_baseline(cfg, qc, kc, vc, args.cpu_heads)
         base["gpu_over_cpu"] = round(tokens_per_s / base["value"], 1)
 

@@ -113,32 +113,31 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 __device__ __forceinline__ int shfl(int x, int src) { return __shfl(x, src, 64); }
 
-// sum of 16 rounded weights (two 8-element vectors) added to acc, two per instruction
+// sum of 16 rounded weights (two 8-element vectors) added to acc, two per
+// instruction, each accumulating straight into the running sum
 __device__ __forceinline__ float row_sum(const bf16x8 (&pb)[2], float acc) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   const b2 one = {(__bf16)1.f, (__bf16)1.f};
-  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const b2 x = {pb[0][2 * e], pb[0][2 * e + 1]};
-    const b2 y = {pb[1][2 * e], pb[1][2 * e + 1]};
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(x, one, s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(y, one, s1, false);
-  }
-  return acc + (s0 + s1);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const b2 x = {pb[h][2 * e], pb[h][2 * e + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+    }
+  return acc;
 }
 __device__ __forceinline__ float row_sum(const f16x8 (&pb)[2], float acc) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const h2 one = {(_Float16)1.f, (_Float16)1.f};
-  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const h2 x = {pb[0][2 * e], pb[0][2 * e + 1]};
-    const h2 y = {pb[1][2 * e], pb[1][2 * e + 1]};
-    s0 = __builtin_amdgcn_fdot2(x, one, s0, false);
-    s1 = __builtin_amdgcn_fdot2(y, one, s1, false);
-  }
-  return acc + (s0 + s1);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const h2 x = {pb[h][2 * e], pb[h][2 * e + 1]};
+      acc = __builtin_amdgcn_fdot2(x, one, acc, false);
+    }
+  return acc;
 }
 
 template <int D, int NW>
