@@ -51,7 +51,9 @@
  * faults surface at the caller's next synchronisation.  Inputs are read-only;
  * outputs may not overlap inputs or the workspace.  Every argument check runs on
  * the host before anything is enqueued, so a nonzero status leaves the outputs
- * untouched.  The library keeps no mutable global state and is reentrant.
+ * untouched.  The library is reentrant.  Two entry points keep per-device state
+ * (noted where they are declared): squad_attn_forward_noalloc (the address of its
+ * scratch array) and squad_block_forward (a rocBLAS handle).
  */
 #ifndef SQUAD_H
 #define SQUAD_H
@@ -74,8 +76,13 @@ enum squad_status {
   SQUAD_ERR_ALIAS = 4,       /* an output overlaps an input or the workspace         */
   SQUAD_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned                */
   SQUAD_ERR_WORKSPACE = 6,   /* workspace null or smaller than required             */
-  SQUAD_ERR_HIP = 7          /* a HIP call failed (no device, launch failure)        */
+  SQUAD_ERR_HIP = 7,         /* a HIP call failed (no device, launch failure)        */
+  SQUAD_ERR_SCRATCH = 8      /* squad_attn_forward_noalloc: one (batch, head)'s local
+                                output exceeds SQUAD_NOALLOC_SCRATCH_BYTES          */
 };
+
+/* Bytes of device scratch squad_attn_forward_noalloc keeps per device. */
+#define SQUAD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum squad_dtype { SQUAD_DTYPE_F32 = 0, SQUAD_DTYPE_BF16 = 1 };
 
@@ -125,6 +132,30 @@ int squad_attn_forward_global(const void* q, const void* k,
  * invalid. */
 size_t squad_attn_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads,
                                  int32_t batch, int32_t head_dim, int32_t dtype);
+
+/*
+ * squad_attn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, layout, precision and statuses as squad_attn_forward, without the
+ * workspace: the local output lives in a device array of
+ * SQUAD_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one copy per device,
+ * held until the process ends.  When batch * heads * G * Wn * head_dim elements of
+ * the local output (fp16 for bf16 calls, fp32 for fp32) exceed it, the call runs
+ * the two passes over slices of the heads of one batch element at a time, one
+ * after the other on `stream`; one (batch, head)'s local output must fit
+ * (SQUAD_ERR_SCRATCH otherwise: at head_dim 128, G * Wn <= 262,144 cells in bf16,
+ * 131,072 in fp32).  Results are bit-identical to squad_attn_forward's.  Nothing
+ * in the scratch needs to start at zero (every cell the global pass reads is
+ * written by the local pass first).  Every call on a device shares that device's
+ * array: calls that overlap in time on one device (different streams, or
+ * different host threads without ordering) race on it and must not be issued.
+ * The first call on a device looks up the array's address (hipGetSymbolAddress)
+ * and keeps it; no call allocates or frees memory.
+ */
+int squad_attn_forward_noalloc(const void* q, const void* k, const void* v,
+                               const int32_t grid[3], const int32_t tile[3], int32_t heads,
+                               void* out, int32_t batch, int32_t head_dim, int32_t dtype,
+                               float scale, squad_stream_t stream);
 
 /*
  * Training.  The distillation the pages run (flow-matching SFT, then DMD2;

@@ -44,6 +44,7 @@ __all__ = [
     "squad_kpass_backward",
     "squad_block_workspace_size",
     "squad_block_forward",
+    "squad_attn_forward_noalloc",
     "DTYPE_CODES",
 ]
 
@@ -145,6 +146,20 @@ def squad_attn_forward(q, k, v, grid, tile, heads=None, out=None, scale=None, wo
         _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(out), B, d,
         DTYPE_CODES[q.dtype], _scale(scale), _ptr(workspace), ws_bytes, _stream(stream, q.device))
     _check(st, "squad_attn_forward")
+    return out
+
+
+def squad_attn_forward_noalloc(q, k, v, grid, tile, heads=None, out=None, scale=None, stream=None):
+    """squad_attn_forward without a workspace: the library keeps the local output in
+    its own per-device scratch array (for callers that cannot allocate, such as
+    code under graph capture).  Pass `out` to make the call allocate nothing at
+    all; calls that overlap in time on one device must not be issued."""
+    q, k, v, B, n, Hh, d = _token_inputs(q, k, v, grid, heads)
+    out = _out_like(out, q)
+    st = _lib.lib().squad_attn_forward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(out), B, d,
+        DTYPE_CODES[q.dtype], _scale(scale), _stream(stream, q.device))
+    _check(st, "squad_attn_forward_noalloc")
     return out
 
 

@@ -16,7 +16,12 @@ STATUS_NAMES = {
     5: "SQUAD_ERR_ALIGN",
     6: "SQUAD_ERR_WORKSPACE",
     7: "SQUAD_ERR_HIP",
+    8: "SQUAD_ERR_SCRATCH",
 }
+
+# bytes of device scratch squad_attn_forward_noalloc holds per device
+# (SQUAD_NOALLOC_SCRATCH_BYTES in include/squad.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = [
     "squad_status_string",
@@ -45,6 +50,7 @@ EXPORTS = [
     "squad_kpass_train_workspace_size",
     "squad_kpass_forward_train",
     "squad_kpass_backward",
+    "squad_attn_forward_noalloc",
 ]
 
 _lib = None
@@ -61,6 +67,8 @@ def _declare(lib):
     lib.squad_status_string.restype = ctypes.c_char_p
     lib.squad_attn_forward.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, P, SZ, P]
     lib.squad_attn_forward.restype = ctypes.c_int
+    lib.squad_attn_forward_noalloc.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, P]
+    lib.squad_attn_forward_noalloc.restype = ctypes.c_int
     lib.squad_attn_forward_local.argtypes = [P, P, P, I3, I3, I32, I32, I32, I32, F, P, SZ, P]
     lib.squad_attn_forward_local.restype = ctypes.c_int
     lib.squad_attn_forward_global.argtypes = [P, P, I3, I3, I32, P, I32, I32, I32, F, P, SZ, P]

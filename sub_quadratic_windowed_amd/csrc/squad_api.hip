@@ -209,6 +209,9 @@ const char* squad_status_string(int status) {
     case SQUAD_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case SQUAD_ERR_WORKSPACE: return "workspace null or smaller than squad_attn_workspace_size()";
     case SQUAD_ERR_HIP: return "HIP error (no device, or a launch failed)";
+    case SQUAD_ERR_SCRATCH:
+      return "the local output of one (batch, head) exceeds the no-allocation entry point's "
+             "scratch (SQUAD_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -282,15 +285,16 @@ int forward_local(const void* q, const void* k, const void* v, const Geo& g, int
 }
 
 // Global pass of the forward: units = offset groups, rows = windows; the value
-// stream is the local output in the workspace; the output goes to token order.
+// stream is the local output in the workspace; the output goes to token order
+// (out_ts: elements from one output token's row to the next, heads * d if 0).
 int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_t heads, int32_t batch,
                    int32_t head_dim, int32_t dtype, float scale, const void* workspace, hipStream_t s,
-                   float* lse = nullptr, int64_t in_ts = 0) {
+                   float* lse = nullptr, int64_t in_ts = 0, int64_t out_ts = 0) {
   AttnArgs a = attn_args(q, k, workspace, out, (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, scale);
   a.lse = lse;
   a.mqk = token_map(g, heads, head_dim, false, in_ts);
   a.mv = group_major_map(g, heads, head_dim, false);
-  a.mo = token_map(g, heads, head_dim, false);
+  a.mo = token_map(g, heads, head_dim, false, out_ts);
   set_cut(a, g, false);
   return run_attn(a, head_dim, dtype, s, VType::kF16ToBf16);
 }
@@ -1192,6 +1196,83 @@ int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, con
   }
   if (st) return st;
   return gemm_xwt(hnd, attn, w_out, y, M, hidden, hidden, dtype);
+}
+
+// ---- the forward for callers that cannot allocate (graph capture, serving loops):
+// its local output lives in a file-scope device array instead of a caller's
+// workspace.  Each device holds its own copy until the process ends; host code
+// uses the address hipGetSymbolAddress gives for the current device, never the
+// array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[SQUAD_NOALLOC_SCRATCH_BYTES];
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // per device: the device address of `scratch`
+
+// The current device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.
+int scratch_address(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SQUAD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SQUAD_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return SQUAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int squad_attn_forward_noalloc(const void* q, const void* k, const void* v, const int32_t grid[3],
+                               const int32_t tile[3], int32_t heads, void* out, int32_t batch,
+                               int32_t head_dim, int32_t dtype, float scale, squad_stream_t stream) {
+  Geo g;
+  size_t bytes = 0;
+  int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true);
+  if (st) return st;
+  const void* in[3] = {q, k, v};
+  st = check_ptrs(in, 3, out, bytes);
+  if (st) return st;
+  if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
+  const size_t esz = elem_bytes(dtype);
+  // the local output of one (batch, head): G * Wn rows of head_dim elements
+  const size_t per_head = (size_t)g.G * (size_t)g.Wn * (size_t)head_dim * esz;
+  if (per_head > SQUAD_NOALLOC_SCRATCH_BYTES) return SQUAD_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((size_t)batch * (size_t)heads * per_head <= SQUAD_NOALLOC_SCRATCH_BYTES) {
+    st = forward_local(q, k, v, g, heads, batch, head_dim, dtype, scale, ws, s);
+    if (st) return st;
+    return forward_global(q, k, out, g, heads, batch, head_dim, dtype, scale, ws, s);
+  }
+  // slices of at most `hs` heads of one batch element, one after the other on the
+  // stream (each slice's global pass has read the scratch before the next local
+  // pass writes it); the token maps keep the full row stride heads * head_dim
+  const int64_t ts = (int64_t)heads * head_dim;
+  const int32_t hs = (int32_t)std::min<size_t>(SQUAD_NOALLOC_SCRATCH_BYTES / per_head, (size_t)heads);
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t h0 = 0; h0 < heads; h0 += hs) {
+      const int32_t hn = std::min(hs, heads - h0);
+      const size_t off = ((size_t)b * (size_t)g.n * (size_t)ts + (size_t)h0 * (size_t)head_dim) * esz;
+      const char* qs = (const char*)q + off;
+      const char* ks = (const char*)k + off;
+      st = forward_local(qs, ks, (const char*)v + off, g, hn, 1, head_dim, dtype, scale, ws, s, nullptr, ts);
+      if (st) return st;
+      st = forward_global(qs, ks, (char*)out + off, g, hn, 1, head_dim, dtype, scale, ws, s, nullptr, ts, ts);
+      if (st) return st;
+    }
+  return SQUAD_OK;
 }
 
 int squad_debug_mfma_probe(float* out, int32_t blocks, int32_t iters, squad_stream_t stream) {

@@ -15,7 +15,7 @@ import sub_quadratic_windowed_amd as sq
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "squad.h")
 
-OK, INVALID, SHAPE, UNSUP, ALIAS, ALIGN, WORKSPACE, HIP = range(8)
+OK, INVALID, SHAPE, UNSUP, ALIAS, ALIGN, WORKSPACE, HIP, SCRATCH = range(9)
 
 
 def header_functions():
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings():
     lib = _lib.lib()
-    for s in range(8):
+    for s in range(9):
         assert lib.squad_status_string(s).decode() != "unknown status"
     assert lib.squad_status_string(99).decode() == "unknown status"
 
@@ -79,6 +79,34 @@ def fwd(q=A, k=B, v=C, grid=(4, 8, 8), tile=(1, 4, 4), heads=2, out=O, batch=1, 
 ])
 def test_forward_rejects_bad_arguments(kw, status):
     assert fwd(**kw) == status
+
+
+def fwd_noalloc(q=A, k=B, v=C, grid=(4, 8, 8), tile=(1, 4, 4), heads=2, out=O, batch=1, d=64, dtype=1,
+                scale=0.0):
+    return _lib.lib().squad_attn_forward_noalloc(
+        ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), _lib.int3(grid), _lib.int3(tile), heads,
+        ctypes.c_void_p(out), batch, d, dtype, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), INVALID), (dict(out=0), INVALID), (dict(heads=0), INVALID), (dict(tile=(5, 4, 4)), SHAPE),
+    (dict(d=96), UNSUP), (dict(dtype=2), UNSUP), (dict(q=A + 8), ALIGN), (dict(out=B + 64), ALIAS),
+    (dict(scale=float("nan")), INVALID),
+    # one (batch, head)'s local output past the 64 MiB scratch: 266,240 cells x 128 x 2 bytes
+    (dict(grid=(64, 64, 65), tile=(4, 8, 5), heads=1, d=128), SCRATCH),
+    # fp32: 262,144 cells x 128 x 4 bytes = 128 MiB
+    (dict(grid=(64, 64, 64), tile=(4, 8, 8), heads=1, d=128, dtype=0), SCRATCH),
+])
+def test_noalloc_rejects_bad_arguments(kw, status):
+    """The checks run on the host before the scratch is looked up or anything is
+    enqueued (no device here)."""
+    assert fwd_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SQUAD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_other_entry_points_reject_bad_arguments():
