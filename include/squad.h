@@ -51,9 +51,11 @@
  * faults surface at the caller's next synchronisation.  Inputs are read-only;
  * outputs may not overlap inputs or the workspace.  Every argument check runs on
  * the host before anything is enqueued, so a nonzero status leaves the outputs
- * untouched.  The library is reentrant.  Two entry points keep per-device state
- * (noted where they are declared): squad_attn_forward_noalloc (the address of its
- * scratch array) and squad_block_forward (a rocBLAS handle).
+ * untouched.  The library is reentrant.  Exceptions, noted where they are
+ * declared: squad_attn_forward_noalloc keeps the address of its own scratch array
+ * per device, and squad_blas_create creates a rocBLAS handle (which owns whatever
+ * device memory rocBLAS allocates for it) for the caller to pass to
+ * squad_block_forward and to release with squad_blas_destroy.
  */
 #ifndef SQUAD_H
 #define SQUAD_H
@@ -66,6 +68,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* squad_stream_t; /* the same type as hipStream_t */
+typedef struct _rocblas_handle* squad_blas_t;  /* the same type as rocblas_handle */
 
 enum squad_status {
   SQUAD_OK = 0,
@@ -229,20 +232,26 @@ int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]);
  *                      the comparator)
  *   y   = a w_out^T   (w_out [hidden, hidden]; y [batch, n, hidden])
  * hidden = heads * head_dim.  The projections are plain GEMMs on rocBLAS (fp32
- * accumulation, outputs rounded to `dtype`); the attention kernels read q, k and v
- * in place from the projection's output rows (row stride 3 hidden).  `workspace`
- * holds qkv, the operator's workspace and a (squad_block_workspace_size bytes).
- * Statuses as for squad_attn_forward, plus SQUAD_ERR_SHAPE when n * 3 * hidden
- * reaches 2^31.  Unlike every other entry point, the first call on a device
- * creates that device's rocBLAS handle, which allocates its own device memory
- * once, kept until the process ends.
+ * accumulation, outputs rounded to `dtype`) on the caller's handle `blas`, whose
+ * stream this call sets to `stream`; the attention kernels read q, k and v in place
+ * from the projection's output rows (row stride 3 hidden).  `workspace` holds qkv,
+ * the operator's workspace and a (squad_block_workspace_size bytes).  Statuses as
+ * for squad_attn_forward (SQUAD_ERR_INVALID_ARG for a null handle), plus
+ * SQUAD_ERR_SHAPE when n * 3 * hidden reaches 2^31.  The call keeps no state of
+ * its own; rocBLAS may allocate device memory on the handle, which the handle owns.
+ *
+ * squad_blas_create: a rocBLAS handle on the current device for squad_block_forward
+ * (SQUAD_ERR_HIP if rocBLAS cannot create one); squad_blas_destroy releases it and
+ * whatever rocBLAS allocated for it.
  */
+int squad_blas_create(squad_blas_t* handle);
+int squad_blas_destroy(squad_blas_t handle);
 size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads, int32_t batch,
                                   int32_t head_dim, int32_t dtype);
 int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, const int32_t grid[3],
                         const int32_t tile[3], int32_t heads, void* y, int32_t batch, int32_t head_dim,
-                        int32_t dtype, float scale, int32_t dense, void* workspace, size_t workspace_bytes,
-                        squad_stream_t stream);
+                        int32_t dtype, float scale, int32_t dense, squad_blas_t blas, void* workspace,
+                        size_t workspace_bytes, squad_stream_t stream);
 
 /*
  * More than two passes.  The pages name composing more than two passes as future

@@ -44,6 +44,7 @@ __all__ = [
     "squad_kpass_backward",
     "squad_block_workspace_size",
     "squad_block_forward",
+    "BlasHandle",
     "squad_attn_forward_noalloc",
     "DTYPE_CODES",
 ]
@@ -270,11 +271,46 @@ def squad_block_workspace_size(grid, tile, heads, batch, head_dim, dtype):
                                                      int(head_dim), code))
 
 
+class BlasHandle:
+    """A rocBLAS handle from squad_blas_create for squad_block_forward, created on
+    the current device and released with squad_blas_destroy when closed or
+    collected."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(_lib.lib().squad_blas_create(ctypes.byref(h)), "squad_blas_create")
+        self.ptr = h
+
+    def close(self):
+        if self.ptr is not None and self.ptr.value:
+            _lib.lib().squad_blas_destroy(self.ptr)
+        self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_blas_handles = {}
+
+
+def _blas_for(device):
+    """The binding's own handle for `device` (one per device, kept by this module)."""
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    if key not in _blas_handles:
+        with torch.cuda.device(key):
+            _blas_handles[key] = BlasHandle()
+    return _blas_handles[key]
+
+
 def squad_block_forward(x, w_qkv, w_out, grid, tile, heads, y=None, scale=None, dense=False, workspace=None,
-                        stream=None):
+                        stream=None, blas=None):
     """The attention block: y = SQuad(x w_qkv^T split into q, k, v) w_out^T (dense=True:
     full attention instead).  x [batch, n, hidden], w_qkv [3 hidden, hidden], w_out
-    [hidden, hidden]; returns y [batch, n, hidden]."""
+    [hidden, hidden]; returns y [batch, n, hidden].  `blas`: a BlasHandle (by default
+    the binding's own handle for x's device)."""
     x = _tensor(x, "x", 3)
     B, n, hidden = x.shape
     Hh = int(heads)
@@ -297,7 +333,7 @@ def squad_block_forward(x, w_qkv, w_out, grid, tile, heads, y=None, scale=None, 
     workspace = _workspace(workspace, squad_block_workspace_size(grid, tile, Hh, B, d, x.dtype), x.device)
     st = _lib.lib().squad_block_forward(
         _ptr(x), _ptr(w_qkv), _ptr(w_out), _lib.int3(grid), _lib.int3(tile), Hh, _ptr(y), B, d,
-        DTYPE_CODES[x.dtype], _scale(scale), 1 if dense else 0, _ptr(workspace),
+        DTYPE_CODES[x.dtype], _scale(scale), 1 if dense else 0, (blas or _blas_for(x.device)).ptr, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, x.device))
     _check(st, "squad_block_forward")
     return y

@@ -51,6 +51,8 @@ EXPORTS = [
     "squad_kpass_forward_train",
     "squad_kpass_backward",
     "squad_attn_forward_noalloc",
+    "squad_blas_create",
+    "squad_blas_destroy",
 ]
 
 _lib = None
@@ -89,7 +91,11 @@ def _declare(lib):
     lib.squad_debug_kpass_offsets.restype = ctypes.c_int
     lib.squad_block_workspace_size.argtypes = [I3, I3, I32, I32, I32, I32]
     lib.squad_block_workspace_size.restype = SZ
-    lib.squad_block_forward.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, I32, P, SZ, P]
+    lib.squad_block_forward.argtypes = [P, P, P, I3, I3, I32, P, I32, I32, I32, F, I32, P, P, SZ, P]
+    lib.squad_blas_create.argtypes = [ctypes.POINTER(P)]
+    lib.squad_blas_create.restype = ctypes.c_int
+    lib.squad_blas_destroy.argtypes = [P]
+    lib.squad_blas_destroy.restype = ctypes.c_int
     lib.squad_block_forward.restype = ctypes.c_int
     lib.squad_debug_mfma_probe.argtypes = [P, I32, I32, P]
     lib.squad_debug_mfma_probe.restype = ctypes.c_int

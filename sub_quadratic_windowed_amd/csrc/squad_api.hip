@@ -1076,9 +1076,6 @@ int squad_debug_kpass_offsets(const int32_t grid[3], const int32_t* tiles, int32
 // the projection's output rows)
 namespace {
 
-std::mutex g_blas_mu;
-rocblas_handle g_blas[64];
-
 // y[M, N] = x[M, K] w[N, K]^T, all row-major (rocBLAS is column-major: y^T = w x^T)
 int gemm_xwt(rocblas_handle hnd, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
              int32_t dtype) {
@@ -1118,6 +1115,19 @@ int block_layout(const Geo& g, int32_t heads, int32_t batch, int32_t head_dim, i
 
 extern "C" {
 
+int squad_blas_create(squad_blas_t* handle) {
+  if (!handle) return SQUAD_ERR_INVALID_ARG;
+  rocblas_handle h = nullptr;
+  if (rocblas_create_handle(&h) != rocblas_status_success || !h) return SQUAD_ERR_HIP;
+  *handle = (squad_blas_t)h;
+  return SQUAD_OK;
+}
+
+int squad_blas_destroy(squad_blas_t handle) {
+  if (!handle) return SQUAD_ERR_INVALID_ARG;
+  return rocblas_destroy_handle((rocblas_handle)handle) == rocblas_status_success ? SQUAD_OK : SQUAD_ERR_HIP;
+}
+
 size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], int32_t heads, int32_t batch,
                                   int32_t head_dim, int32_t dtype) {
   Geo g;
@@ -1131,8 +1141,8 @@ size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], 
 
 int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, const int32_t grid[3],
                         const int32_t tile[3], int32_t heads, void* y, int32_t batch, int32_t head_dim,
-                        int32_t dtype, float scale, int32_t dense, void* workspace, size_t workspace_bytes,
-                        squad_stream_t stream) {
+                        int32_t dtype, float scale, int32_t dense, squad_blas_t blas, void* workspace,
+                        size_t workspace_bytes, squad_stream_t stream) {
   Geo g;
   size_t bytes = 0;
   int st = check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true);
@@ -1147,7 +1157,7 @@ int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, con
   if ((int64_t)batch * g.n >= (int64_t(1) << 31) || 3 * hidden >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   const size_t wq_bytes = (size_t)3 * hidden * hidden * elem_bytes(dtype);
   const size_t wo_bytes = (size_t)hidden * hidden * elem_bytes(dtype);
-  if (!x || !w_qkv || !w_out || !y) return SQUAD_ERR_INVALID_ARG;
+  if (!x || !w_qkv || !w_out || !y || !blas) return SQUAD_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < lay.total) return SQUAD_ERR_WORKSPACE;
   if (misaligned(x) || misaligned(w_qkv) || misaligned(w_out) || misaligned(y) || misaligned(workspace))
     return SQUAD_ERR_ALIGN;
@@ -1157,11 +1167,7 @@ int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, con
     return SQUAD_ERR_ALIAS;
   if (!isfinite(scale)) return SQUAD_ERR_INVALID_ARG;
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SQUAD_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_blas_mu);
-  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) return SQUAD_ERR_HIP;
-  rocblas_handle hnd = g_blas[dev];
+  rocblas_handle hnd = (rocblas_handle)blas;
   hipStream_t s = (hipStream_t)stream;
   if (rocblas_set_stream(hnd, s) != rocblas_status_success) return SQUAD_ERR_HIP;
 

@@ -398,10 +398,12 @@ def test_block_entry_point_rejects_bad_arguments():
     hidden = 128
     assert need >= 256 * 3 * hidden * 2 + 256 * hidden * 2   # qkv and the attention output, bf16
 
-    def blk(x=X, wq=WQ, wo=WO, y=Y, dense=0, ws=WS, wb=1 << 30, d=64, grid=g, heads=2):
+    # a fake, never-used rocBLAS handle: every argument check fires before the handle is touched
+    def blk(x=X, wq=WQ, wo=WO, y=Y, dense=0, ws=WS, wb=1 << 30, d=64, grid=g, heads=2, blas=0x60000000):
         return lib.squad_block_forward(p(x), p(wq), p(wo), grid, t, heads, p(y), 1, d, 1, ctypes.c_float(0), dense,
-                                       p(ws), wb, None)
+                                       p(blas), p(ws), wb, None)
     assert blk(x=0) == INVALID
+    assert blk(blas=0) == INVALID
     assert blk(dense=2) == INVALID
     assert blk(d=96) == UNSUP
     assert blk(y=X) == ALIAS

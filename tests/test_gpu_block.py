@@ -88,3 +88,21 @@ def test_block_at_the_5b_dit_shape_equals_its_parts():
     assert torch.isfinite(y).all()
     assert float(diff.max()) <= 3e-2 * max(1.0, float(y2.float().abs().max()))
     assert float(diff.mean()) <= 2e-3
+
+
+def test_block_on_a_caller_handle():
+    """squad_block_forward on a rocBLAS handle the caller creates (squad_blas_create)
+    and releases (squad_blas_destroy) gives the same bits as on the binding's own
+    handle, also on a side stream."""
+    grid, tile, Hh, d = (4, 6, 10), (2, 3, 5), 2, 64
+    x, wqkv, wo = block_inputs(1, 240, Hh * d, torch.bfloat16, 53)
+    ref = sq.squad_block_forward(x, wqkv, wo, grid, tile, Hh)
+    torch.cuda.synchronize()
+    h = sq.BlasHandle()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y = torch.empty_like(x)
+    sq.squad_block_forward(x, wqkv, wo, grid, tile, Hh, y=y, blas=h, stream=side)
+    side.synchronize()
+    h.close()
+    assert torch.equal(y, ref)

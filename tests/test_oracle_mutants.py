@@ -40,6 +40,8 @@ MUTANTS = {
         so, "global_pass", lambda q, k, v, g, t, s=None: so.local_pass(q, k, v, g, t, s)),
     "global pass fed v instead of the local output": lambda mp: mp.setattr(
         so, "squad_forward", lambda q, k, v, g, t, s=None: so.global_pass(q, k, v, g, t, s)),
+    "q and k swapped in the global pass": lambda mp: mp.setattr(
+        so, "global_pass", (lambda f: (lambda q, k, v, g, t, s=None: f(k, q, v, g, t, s)))(so.global_pass)),
     "local pass skipped": lambda mp: mp.setattr(
         so, "local_pass", lambda q, k, v, g, t, s=None: np.asarray(v, np.float64)),
     "softmax over the query axis": lambda mp: mp.setattr(so, "softmax_attention", _swap_axes_softmax),
