@@ -309,12 +309,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bool qok = present(qi);
   const uint32_t qr = load_row(qi);
 
-  // query and upstream-gradient fragments; D = <dout, o> over this lane's dims
+  // query and upstream-gradient fragments; D = <dout, o> over this lane's dims,
+  // unless the pass above already left D for these rows
   bf16x8 qf[D / 16], df[D / 16];
   load_row_frags<D, false>(qg + bytes16(a.mqk.row_off(qr)), half, qf);
   load_row_frags<D, false>(dg + bytes16(a.mdo.row_off(qr)), half, df);
+  const size_t row_id = (size_t)p.u * L + qi;
   float dsum = 0.f;
-  {
+  if (a.dsum_ready) {
+    dsum = qok ? a.dsum[row_id] : 0.f;
+  } else {
     const char* orow = og + bytes16(a.mo.row_off(qr)) + half * 16;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -322,8 +326,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsum = fmaf((float)df[kk][e], elem<OF16>(&raw, e), dsum);
     }
+    dsum = sum_halves(dsum);
   }
-  dsum = sum_halves(dsum);
   // fp16 values (the global pass reads the local output): dP^T runs on fp16 MFMAs
   // with the row's dout scaled by a power of two into fp16 range (max |dout| to
   // [2^13, 2^14)), undone on the fp32 product, so V needs no conversion per block
@@ -346,9 +350,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int e = 0; e < 8; ++e) dh[kk][e] = (_Float16)((float)df[kk][e] * up);
   }
-  const size_t row_id = (size_t)p.u * L + qi;
   const float lse = qok ? a.lse[row_id] : 0.f;
-  if (qok && half == 0) a.dsum[row_id] = dsum;
+  if (!a.dsum_ready && qok && half == 0) a.dsum[row_id] = dsum;
 
   Layout<D, NW> lay;
   lay.init(lane, wave);
@@ -664,6 +667,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (qb < nqb) step(qb, std::integral_constant<int, 0>{}, std::false_type{});
   if (qb + 1 < nqb) step(qb + 1, std::integral_constant<int, 1>{}, std::false_type{});
 
+  // D of the pass below for this wave's value rows, <dv_j, v_j>, with dv_j rounded
+  // to bf16 as it is stored (the pass below forms its products from those values)
+  // and v_j the own row in LDS, as rounded for the products; read from LDS before
+  // the stores below reuse those rows
+  if (a.dsum_next && active) {
+    float dn = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // dims 32 mt + 8 g + 4 half + (0..3): chunk 4 mt + g, elements 4 half + (0..3)
+        const uint2 raw = *(const uint2*)(vrow_lds + (((uint32_t)(4 * mt + g) ^ vxor) << 4) + 8 * half);
+        const bf16x4 vv = __builtin_bit_cast(bf16x4, raw);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dn = fmaf((float)(__bf16)dva[mt][4 * g + e], (float)vv[e], dn);
+      }
+    dn = sum_halves(dn);
+    const uint32_t bh = p.b * a.heads + p.h;
+    if (kok && half == 0) a.dsum_next[((size_t)kj * a.BH + bh) * a.U + p.s] = dn;
+  }
   // (every wave is past the last step's barrier: wave w stages its stores in its
   // own 32 rows of the V block)
   if (active) {

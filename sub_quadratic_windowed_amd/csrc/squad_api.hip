@@ -302,7 +302,7 @@ int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_
 // ---- training: the forward's saved state and the backward's scratch, in one
 // workspace (sections 256-byte aligned)
 struct TrainLayout {
-  size_t o1, lse_l, lse_g, dsum, do1, dq_acc, dk_acc, total;
+  size_t o1, lse_l, lse_g, dsum, dsum_l, do1, dq_acc, dk_acc, total;
 };
 
 TrainLayout train_layout(const Geo& g, int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
@@ -315,7 +315,8 @@ TrainLayout train_layout(const Geo& g, int32_t heads, int32_t batch, int32_t hea
   t.lse_l = al(t.o1 + bh * cells * head_dim * esz);
   t.lse_g = al(t.lse_l + bh * cells * 4);
   t.dsum = al(t.lse_g + bh * cells * 4);
-  t.do1 = al(t.dsum + bh * cells * 4);
+  t.dsum_l = al(t.dsum + bh * cells * 4);
+  t.do1 = al(t.dsum_l + bh * cells * 4);
   size_t end = al(t.do1 + bh * cells * head_dim * esz);
   // bf16 calls sum dq and dk over the passes in fp32 (fp32 calls use dq and dk)
   t.dq_acc = t.dk_acc = 0;
@@ -748,6 +749,11 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   ag.mdq = ag.mqk; ag.mdk = ag.mqk;
   ag.dv = ws + t.do1; ag.mdv = ag.mv;
   ag.final_pass = 0;
+  // the global pass's key side (bf16, when it runs as the two kinds) also leaves D
+  // of the local pass, <do1, o1>, for the rows of every window; the local pass's
+  // query side then reads it instead of the local output
+  const bool hand_off = bf16 && !bwd_bf16_fused(ag.L, ag.cut.on) && !bwd_bf16_fused(g.Wn, g.cut);
+  if (hand_off) ag.dsum_next = (float*)(ws + t.dsum_l);
   st = run_bwd(ag, head_dim, dtype, BwdTypes{true, false}, s);
   if (st) return st;
 
@@ -760,7 +766,8 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   al.mo = group_major_map(g, heads, head_dim, true);
   al.mdo = al.mo;
   al.lse = (const float*)(ws + t.lse_l);
-  al.dsum = (float*)(ws + t.dsum);
+  al.dsum = (float*)(ws + (hand_off ? t.dsum_l : t.dsum));
+  al.dsum_ready = hand_off ? 1 : 0;
   al.dq = dq; al.dk = dk; al.dq_acc = dq_acc; al.dk_acc = dk_acc;
   al.mdq = al.mqk; al.mdk = al.mqk;
   al.dv = dv; al.mdv = al.mqk;

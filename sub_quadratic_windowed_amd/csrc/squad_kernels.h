@@ -101,6 +101,11 @@ struct BwdArgsT {
   Map mqk, mv, mo, mdo;
   const float* lse;   // [u * L + r]
   float* dsum;        // [u * L + r]: D, written by kind A, read by kind B
+  uint32_t dsum_ready;  // nonzero: dsum already holds D (kind A reads it instead of forming it)
+  // optional (kind B, two-pass global pass): D of the pass below for this pass's
+  // value rows, <dv_j, v_j>, at [(row * BH + bh) * U + unit] (the lower pass's
+  // units are this pass's rows and its rows this pass's units)
+  float* dsum_next;
   void* dq;           // kind A, final pass: dq in the call's dtype (token order, mdq)
   void* dk;           // kind B, final pass: dk
   float* dq_acc;      // fp32 accumulators (mdq / mdk offsets)
