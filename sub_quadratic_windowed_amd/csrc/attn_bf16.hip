@@ -183,9 +183,13 @@ __device__ __forceinline__ uint32_t half_bits(uint32_t rows, uint32_t h) {
 // tiles) are neither keys nor stored queries.  With the row tables (TAB) their
 // presence bits are formed once per workgroup into LDS; without them, for each key
 // block one step ahead, with one ballot.
-template <int D, int NW, typename VT, typename OT, bool TAB, bool CUT = false, typename Args = AttnArgs>
+template <int D, int NW, typename VT, typename OT, bool TAB, bool CUT = false, typename Args = AttnArgs,
+          bool WIDE = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void attn16_kernel(Args a) {
   typedef Cfg<D, NW> C;
+  // wide maps (row offsets in head rows) form their rows' offsets per load
+  static_assert(!(WIDE && TAB), "the row tables hold 32-bit byte offsets");
+  typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type boff_t;
   typedef typename Vec<VT>::x8 vx8;
   typedef typename Vec<VT>::x4 vx4;
   typedef typename Vec<OT>::x4 ox4;
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   bf16x8 qf[D / 16];
   {
     const uint32_t qrow = CUT ? (present(q0 + l32) ? q0 + l32 : 0) : min(q0 + l32, L - 1);
-    const __bf16* qr = qg + a.mqk.row_off(qrow) + half * 8;
+    const __bf16* qr = qg + row_elems<WIDE, D>(a.mqk.row_off(qrow)) + half * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(qr + kk * 16);
   }
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
   // Loads of one block are prepared (row offsets located, lanes' 32-bit element
   // offsets formed) one step before they are issued, so the shuffles and the
   // address arithmetic stay off the path between a block's barrier and its MFMAs.
-  uint32_t pk[C::VPW], pv[C::VPW];
+  boff_t pk[C::VPW], pv[C::VPW];
   auto prep_block = [&](uint32_t kb, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     if constexpr (TAB) {
@@ -338,8 +342,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
         const int ins = wave + i * NW;
         const uint32_t krow = C::KRPI * ins + krow0;
         const uint32_t kchunk = kslot ^ (krow & (C::CPR - 1));
-        pk[i] = bytes16(shfl(ko, krow & 31)) + kchunk * 16;
-        pv[i] = bytes16(shfl(vo, (4 * C::GPI * ins + vrow0) & 31)) + vcol * 16;
+        pk[i] = row_bytes16<WIDE, D>(shfl(ko, krow & 31)) + kchunk * 16;
+        pv[i] = row_bytes16<WIDE, D>(shfl(vo, (4 * C::GPI * ins + vrow0) & 31)) + vcol * 16;
       }
     }
   };
@@ -353,6 +357,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       const int ins = wave + i * NW;
       if (C::VPW * NW != C::VINS && ins >= C::VINS) break;
       // uniform base + unsigned 32-bit byte offset: one offset register per load
+      // (wide maps: a 64-bit offset)
       __builtin_amdgcn_global_load_lds((const void*)((const char*)kg + pk[i]),
                                        (lds_void_t*)(ks + ins * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)((const char*)vg + pv[i]),
@@ -539,13 +544,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) vo
       qok = qok && present(q0 + l32);
     }
     if (a.lse && qok && half == 0) a.lse[(size_t)u * L + q0 + l32] = m_ref + __log2f(lsum);
-    const int32_t oo = qok ? a.mo.row_off(q0 + l32) : -1;
+    const uint32_t oo = qok ? (uint32_t)a.mo.row_off(q0 + l32) : kNoRow;
 #pragma unroll
     for (int i = 0; i < 32 / WR; ++i) {
       const uint32_t r = wrow + i * WR;
-      const int32_t o = shfl(oo, r);
+      const uint32_t o = (uint32_t)shfl((int)oo, r);
       const uint4 x = *(const uint4*)(ostage + r * D + ((wcol ^ (r & (C::CPR - 1))) << 3));
-      if (o >= 0) *(uint4*)(og + o + wcol * 8) = x;
+      if (o != kNoRow) *(uint4*)(og + row_elems<WIDE, D>((int32_t)o) + wcol * 8) = x;
     }
   }
 }
@@ -556,6 +561,14 @@ hipError_t launch(const Args& a, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)groups * 8 * a.nchunks;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   if constexpr (std::is_same<Args, AttnArgs>::value) {
+    if (a.row_unit > 1) {
+      // wide maps: no row tables, presence tested per block (the host marks every
+      // wide call as cut; on a whole tiling every row is present)
+      if (!a.cut.on) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, false, true, AttnArgs, true>), dim3((uint32_t)blocks),
+                         dim3(64 * NW), 0, stream, a);
+      return hipGetLastError();
+    }
     if (a.cut.on) {
       if (a.L <= TABLE_ROWS)
         hipLaunchKernelGGL((attn16_kernel<D, NW, VT, OT, true, true>), dim3((uint32_t)blocks), dim3(64 * NW), 0,
@@ -565,7 +578,7 @@ hipError_t launch(const Args& a, hipStream_t stream) {
                            stream, a);
       return hipGetLastError();
     }
-  } else if (a.cut.on) {
+  } else if (a.cut.on || a.row_unit > 1) {
     return hipErrorInvalidValue;
   }
   if (a.L <= TABLE_ROWS)

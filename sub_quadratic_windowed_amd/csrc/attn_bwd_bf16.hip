@@ -218,7 +218,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 // Store a transposed accumulator tile set: lane l32 (and l32 + 32) owns row l32,
 // holding its element dim 32 mt + 8 (r / 4) + 4 half + r % 4 in acc[mt][r]; `off` is
-// the row's element offset (negative: not stored).  Each value is scaled, then
+// the row's offset under the map (kNoRow: not stored).  Each value is scaled, then
 // written as fp32 (kAccWrite), added to the fp32 accumulator and written back
 // (kAccAdd), or added to it and written as bf16 to outp (kAccFinal; with no
 // accumulator, plainly written).  The rows pass through `stage` (32 rows x D / 2
@@ -226,9 +226,9 @@ __device__ __forceinline__ float sum_halves(float x) {
 // whole row segments, 16 bytes per lane, so a store instruction covers 64 / (D / 8)
 // rows' contiguous bytes rather than 16-byte pieces of 32 rows.  Chunks are
 // XOR-swizzled by row in LDS.
-template <int D>
+template <int D, bool WIDE = false>
 __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], float scale, uint32_t lane,
-                                               uint32_t mode, float* accp, __bf16* outp, int32_t off,
+                                               uint32_t mode, float* accp, __bf16* outp, uint32_t off,
                                                char* stage) {
   constexpr int DR = D / 2;        // fp32 dims per round
   constexpr int NCH = DR / 4;      // 16-byte chunks per staged row
@@ -252,20 +252,21 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], floa
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const uint32_t r = i * RPI + lane / NCH;
-      const int32_t o = __shfl(off, (int)r, 64);
+      const uint32_t o = (uint32_t)__shfl((int)off, (int)r, 64);
       float4 x = *(const float4*)(stage + r * (DR * 4) + ((c ^ (r & (NCH - 1))) << 4));
-      if (o >= 0) {
+      if (o != kNoRow) {
+        const auto oe = row_elems<WIDE, D>((int32_t)o);
         const int d0 = DR * rd + 4 * c;
         if (mode != kAccWrite && accp) {
-          const float4 y = *(const float4*)(accp + o + d0);
+          const float4 y = *(const float4*)(accp + oe + d0);
           x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
         }
         if (mode == kAccFinal) {
           bf16x4 w;
           w[0] = (__bf16)x.x; w[1] = (__bf16)x.y; w[2] = (__bf16)x.z; w[3] = (__bf16)x.w;
-          *(bf16x4*)(outp + o + d0) = w;
+          *(bf16x4*)(outp + oe + d0) = w;
         } else {
-          *(float4*)(accp + o + d0) = x;
+          *(float4*)(accp + oe + d0) = x;
         }
       }
     }
@@ -275,9 +276,12 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], floa
 
 // ---------------------------------------------------------------- kind A: dq (and D)
 
-template <int D, int NW, bool VF16, bool OF16, bool CUT, bool TAB, typename Args = BwdArgs>
+template <int D, int NW, bool VF16, bool OF16, bool CUT, bool TAB, typename Args = BwdArgs, bool WIDE = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_bf16(Args a) {
   typedef BCfg<D, NW> C;
+  // wide maps (row offsets in head rows) form their rows' offsets per load
+  static_assert(!(WIDE && TAB), "the row tables hold 32-bit byte offsets");
+  typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type boff_t;
   constexpr int BM = C::BM;
   UnitPos p;
   if (!unit_pos(a, p)) return;
@@ -312,14 +316,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // query and upstream-gradient fragments; D = <dout, o> over this lane's dims,
   // unless the pass above already left D for these rows
   bf16x8 qf[D / 16], df[D / 16];
-  load_row_frags<D, false>(qg + bytes16(a.mqk.row_off(qr)), half, qf);
-  load_row_frags<D, false>(dg + bytes16(a.mdo.row_off(qr)), half, df);
+  load_row_frags<D, false>(qg + row_bytes16<WIDE, D>(a.mqk.row_off(qr)), half, qf);
+  load_row_frags<D, false>(dg + row_bytes16<WIDE, D>(a.mdo.row_off(qr)), half, df);
   const size_t row_id = (size_t)p.u * L + qi;
   float dsum = 0.f;
   if (a.dsum_ready) {
     dsum = qok ? a.dsum[row_id] : 0.f;
   } else {
-    const char* orow = og + bytes16(a.mo.row_off(qr)) + half * 16;
+    const char* orow = og + row_bytes16<WIDE, D>(a.mo.row_off(qr)) + half * 16;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const uint4 raw = *(const uint4*)(orow + kk * 32);
@@ -373,14 +377,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
-      uint32_t ko, vo;
+      boff_t ko, vo;
       if constexpr (TAB) {
         ko = tab[kb * BN + lay.ld_row[i]];
         vo = tab[BT_ROWS + kb * BN + lay.ld_row[i]];
       } else {
         const uint32_t r = load_row(kb * BN + lay.ld_row[i]);
-        ko = bytes16(a.mqk.row_off(r));
-        vo = bytes16(a.mv.row_off(r));
+        ko = row_bytes16<WIDE, D>(a.mqk.row_off(r));
+        vo = row_bytes16<WIDE, D>(a.mv.row_off(r));
       }
       __builtin_amdgcn_global_load_lds((const void*)(kg + ko + lay.ld_byte[i]),
                                        (lds_void_t*)(ks + ins * 1024), 16, 0, 0);
@@ -480,17 +484,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
              : wave == 1 ? BStage<D, 1, 0>::ptr()
              : wave == 2 ? BStage<D, 2, 0>::ptr() : BStage<D, 0, 1>::ptr();
     const int64_t base = a.mdq.base(p.b, p.h, p.s);
-    store_rows_lds<D>(acc, a.scale, lane, a.final_pass, a.dq_acc + base,
+    store_rows_lds<D, WIDE>(acc, a.scale, lane, a.final_pass, a.dq_acc + base,
                       a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr,
-                      qok ? (int32_t)a.mdq.row_off(qi) : -1, st);
+                      qok ? (uint32_t)a.mdq.row_off(qi) : kNoRow, st);
   }
 }
 
 // ---------------------------------------------------------------- kind B: dk, dv
 
-template <int D, int NW, bool VF16, bool CUT, bool TAB, typename Args = BwdArgs>
+template <int D, int NW, bool VF16, bool CUT, bool TAB, typename Args = BwdArgs, bool WIDE = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_bf16(Args a) {
   typedef BCfg<D, NW> C;
+  static_assert(!(WIDE && TAB), "the row tables hold 32-bit byte offsets");
+  typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type boff_t;
   constexpr int BM = C::BM;
   UnitPos p;
   if (!unit_pos(a, p)) return;
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const bool kok = present(kj);
   const uint32_t kr = load_row(kj);
   bf16x8 kf[D / 16];
-  load_row_frags<D, false>(kg + bytes16(a.mqk.row_off(kr)), half, kf);
+  load_row_frags<D, false>(kg + row_bytes16<WIDE, D>(a.mqk.row_off(kr)), half, kf);
   // the workgroup's own V rows, bf16, in LDS: chunk c of row r at slot c ^ (r % CPR)
   // (read as the B operand of dP, one 16-byte chunk per lane, conflict-free);
   // holding them in registers instead would not leave room for both accumulators
@@ -532,7 +538,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       const uint32_t ch = tid + 64 * NW * i;
       const uint32_t r = ch / C::CPR, cc = ch % C::CPR;
       const uint32_t vr = load_row(p.chunk * BM + r);
-      const uint4 raw = *(const uint4*)(vg + bytes16(a.mv.row_off(vr)) + 16 * cc);
+      const uint4 raw = *(const uint4*)(vg + row_bytes16<WIDE, D>(a.mv.row_off(vr)) + 16 * cc);
       *(bf16x8*)((char*)vown + r * D * 2 + ((cc ^ (r & (C::CPR - 1))) << 4)) = frag<VF16>(raw);
     }
   }
@@ -560,14 +566,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < C::VPW; ++i) {
       const uint32_t ins = wave + i * NW;
-      uint32_t qo, dof;
+      boff_t qo, dof;
       if constexpr (TAB) {
         qo = tab[qb * BN + lay.ld_row[i]];
         dof = tab[BT_ROWS + qb * BN + lay.ld_row[i]];
       } else {
         const uint32_t r = load_row(qb * BN + lay.ld_row[i]);
-        qo = bytes16(a.mqk.row_off(r));
-        dof = bytes16(a.mdo.row_off(r));
+        qo = row_bytes16<WIDE, D>(a.mqk.row_off(r));
+        dof = row_bytes16<WIDE, D>(a.mdo.row_off(r));
       }
       __builtin_amdgcn_global_load_lds((const void*)(qg + qo + lay.ld_byte[i]),
                                        (lds_void_t*)(qs + ins * 1024), 16, 0, 0);
@@ -692,11 +698,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (active) {
     char* st = (char*)vown + wave * 32 * D * 2;
     const int64_t kbase = a.mdk.base(p.b, p.h, p.s), vbase = a.mdv.base(p.b, p.h, p.s);
-    store_rows_lds<D>(dka, a.scale, lane, a.final_pass, a.dk_acc + kbase,
+    store_rows_lds<D, WIDE>(dka, a.scale, lane, a.final_pass, a.dk_acc + kbase,
                       a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr,
-                      kok ? (int32_t)a.mdk.row_off(kj) : -1, st);
-    store_rows_lds<D>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vbase,
-                      kok ? (int32_t)a.mdv.row_off(kj) : -1, st);
+                      kok ? (uint32_t)a.mdk.row_off(kj) : kNoRow, st);
+    store_rows_lds<D, WIDE>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vbase,
+                      kok ? (uint32_t)a.mdv.row_off(kj) : kNoRow, st);
   }
 }
 
@@ -857,9 +863,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int64_t kb0 = a.mdk.base(p.b, p.h, p.s), vb0 = a.mdv.base(p.b, p.h, p.s);
     store_rows_lds<D>(dka, a.scale, lane, a.final_pass, a.dk_acc + kb0,
                       a.final_pass == kAccFinal ? (__bf16*)a.dk + kb0 : nullptr,
-                      rok ? (int32_t)a.mdk.row_off(rj) : -1, own_stage);
+                      rok ? (uint32_t)a.mdk.row_off(rj) : kNoRow, own_stage);
     store_rows_lds<D>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vb0,
-                      rok ? (int32_t)a.mdv.row_off(rj) : -1, own_stage);
+                      rok ? (uint32_t)a.mdv.row_off(rj) : kNoRow, own_stage);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's dS rows are written
   __builtin_amdgcn_s_barrier();
@@ -891,7 +897,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   const int64_t qb0 = a.mdq.base(p.b, p.h, p.s);
   store_rows_lds<D>(acc, a.scale, lane, a.final_pass, a.dq_acc + qb0,
                     a.final_pass == kAccFinal ? (__bf16*)a.dq + qb0 : nullptr,
-                    rok ? (int32_t)a.mdq.row_off(rj) : -1, own_stage);
+                    rok ? (uint32_t)a.mdq.row_off(rj) : kNoRow, own_stage);
 }
 
 template <int D, int NW, bool VF16, bool OF16, typename Args>
@@ -900,6 +906,14 @@ hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;
   const dim3 grid((uint32_t)blocks), block(64 * NW);
   if constexpr (std::is_same<Args, BwdArgs>::value) {
+    if (a.row_unit > 1) {
+      // wide maps: no row tables; the host marks every wide call as cut (on a whole
+      // tiling every row is present)
+      if (!a.cut.on) return hipErrorInvalidValue;
+      if (kind_b) hipLaunchKernelGGL((bwd_dkv_bf16<D, NW, VF16, true, false, BwdArgs, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_bf16<D, NW, VF16, OF16, true, false, BwdArgs, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
     // cut tilings: presence is tested per block (one ballot), with or without the tables
     if (a.cut.on) {
       const bool tab = a.L <= BT_ROWS;
@@ -912,7 +926,7 @@ hipError_t launch(const Args& a, bool kind_b, hipStream_t stream) {
       }
       return hipGetLastError();
     }
-  } else if (a.cut.on) {
+  } else if (a.cut.on || a.row_unit > 1) {
     return hipErrorInvalidValue;
   }
   if (kind_b) {
@@ -958,6 +972,7 @@ namespace {
 template <bool VF16, bool OF16, typename Args>
 hipError_t launch_small(Args a, int head_dim, hipStream_t stream) {
   if (a.L > SMALL_ROWS || a.cut.on) return hipErrorInvalidValue;
+  if (a.row_unit > 1) return hipErrorInvalidValue;   // narrow maps only
   a.nchunks = 1;
   const uint64_t blocks = (uint64_t)((a.units + 7) / 8) * 8;
   if (blocks > 0x7fffffffu) return hipErrorInvalidConfiguration;

@@ -64,6 +64,9 @@ __global__ __launch_bounds__(256) void bwd_dq_f32(Args a) {
 
   UnitPos p;
   if (!unit_pos(a, p)) return;
+  // element offset of row r under map m (narrow maps: elements; wide: head rows)
+  const uint32_t ru = a.row_unit > 1 ? a.row_unit : 1u;
+  auto roff = [&](const auto& m, uint32_t r) -> uint64_t { return row_elems_rt(m.row_off(r), ru); };
   const uint32_t tid = threadIdx.x;
   const uint32_t L = a.L;
   UnitDigits ud;
@@ -84,9 +87,9 @@ __global__ __launch_bounds__(256) void bwd_dq_f32(Args a) {
   float q[C::DL], dof[C::DL], dq[C::DL];
   float dsum = 0.f;
   {
-    const float* qr = qg + (qok ? a.mqk.row_off(qi) : 0) + part * C::DL;
-    const float* dr = dg + (qok ? a.mdo.row_off(qi) : 0) + part * C::DL;
-    const float* orow = og + (qok ? a.mo.row_off(qi) : 0) + part * C::DL;
+    const float* qr = qg + (qok ? roff(a.mqk, qi) : 0) + part * C::DL;
+    const float* dr = dg + (qok ? roff(a.mdo, qi) : 0) + part * C::DL;
+    const float* orow = og + (qok ? roff(a.mo, qi) : 0) + part * C::DL;
 #pragma unroll
     for (int i = 0; i < C::DL; ++i) {
       q[i] = qok ? qr[i] : 0.f;
@@ -115,8 +118,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32(Args a) {
       const uint32_t key = kb * RB + r;
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
       if (present(key)) {
-        kv = *(const float4*)(kg + a.mqk.row_off(key) + cc * 4);
-        vv = *(const float4*)(vg + a.mv.row_off(key) + cc * 4);
+        kv = *(const float4*)(kg + roff(a.mqk, key) + cc * 4);
+        vv = *(const float4*)(vg + roff(a.mv, key) + cc * 4);
       }
       *(float4*)(ks + r * D + cc * 4) = kv;
       *(float4*)(vs + r * D + cc * 4) = vv;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32(Args a) {
   }
 
   if (qok) {
-    const int32_t off = a.mdq.row_off(qi) + part * C::DL;
+    const uint64_t off = roff(a.mdq, qi) + part * C::DL;
     const int64_t base = a.mdq.base(p.b, p.h, p.s);
     float* acc = a.dq_acc + base + off;
 #pragma unroll
@@ -168,6 +171,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32(Args a) {
 
   UnitPos p;
   if (!unit_pos(a, p)) return;
+  // element offset of row r under map m (narrow maps: elements; wide: head rows)
+  const uint32_t ru = a.row_unit > 1 ? a.row_unit : 1u;
+  auto roff = [&](const auto& m, uint32_t r) -> uint64_t { return row_elems_rt(m.row_off(r), ru); };
   const uint32_t tid = threadIdx.x;
   const uint32_t L = a.L;
   UnitDigits ud;
@@ -186,8 +192,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32(Args a) {
   const bool kok = present(kj);
   float k[C::DL], v[C::DL], dk[C::DL], dv[C::DL];
   {
-    const float* kr = kg + (kok ? a.mqk.row_off(kj) : 0) + part * C::DL;
-    const float* vr = vg + (kok ? a.mv.row_off(kj) : 0) + part * C::DL;
+    const float* kr = kg + (kok ? roff(a.mqk, kj) : 0) + part * C::DL;
+    const float* vr = vg + (kok ? roff(a.mv, kj) : 0) + part * C::DL;
 #pragma unroll
     for (int i = 0; i < C::DL; ++i) {
       k[i] = kok ? kr[i] : 0.f;
@@ -219,8 +225,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32(Args a) {
       const uint32_t qr = qb * RB + r;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
       if (present(qr)) {
-        x = *(const float4*)(qg + a.mqk.row_off(qr) + cc * 4);
-        y = *(const float4*)(dg + a.mdo.row_off(qr) + cc * 4);
+        x = *(const float4*)(qg + roff(a.mqk, qr) + cc * 4);
+        y = *(const float4*)(dg + roff(a.mdo, qr) + cc * 4);
       }
       *(float4*)(qs + r * D + cc * 4) = x;
       *(float4*)(ds_ + r * D + cc * 4) = y;
@@ -251,9 +257,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_f32(Args a) {
 
   if (kok) {
     const int64_t kbase = a.mdk.base(p.b, p.h, p.s);
-    const int32_t koff = a.mdk.row_off(kj) + part * C::DL;
+    const uint64_t koff = roff(a.mdk, kj) + part * C::DL;
     float* acc = a.dk_acc + kbase + koff;
-    float* vrow = (float*)a.dv + a.mdv.base(p.b, p.h, p.s) + a.mdv.row_off(kj) + part * C::DL;
+    float* vrow = (float*)a.dv + a.mdv.base(p.b, p.h, p.s) + roff(a.mdv, kj) + part * C::DL;
 #pragma unroll
     for (int e = 0; e < C::DL; e += 4) {
       float4 x = make_float4(dk[e] * a.scale, dk[e + 1] * a.scale, dk[e + 2] * a.scale, dk[e + 3] * a.scale);

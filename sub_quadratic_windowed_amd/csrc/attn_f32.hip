@@ -47,6 +47,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Args a) {
   float* og = (float*)a.o + a.mo.base(b, h, s);
 
   const uint32_t L = a.L;
+  // element offset of row r under map m (narrow maps: elements; wide: head rows)
+  const uint32_t ru = a.row_unit > 1 ? a.row_unit : 1u;
+  auto roff = [&](const auto& m, uint32_t r) -> uint64_t { return row_elems_rt(m.row_off(r), ru); };
   UnitDigits ud;
   if constexpr (CUT) ud = cut_unit_digits(a, s);
   auto present = [&](uint32_t r) -> bool {
@@ -59,7 +62,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Args a) {
 
   float q[DL], acc[DL];
   {
-    const float* qr = qg + (qok ? a.mqk.row_off(qi) : 0) + part * DL;
+    const float* qr = qg + (qok ? roff(a.mqk, qi) : 0) + part * DL;
 #pragma unroll
     for (int i = 0; i < DL; ++i) {
       q[i] = qok ? qr[i] : 0.f;
@@ -83,8 +86,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Args a) {
       const uint32_t key = kb * KB + r;
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
       if (present(key)) {
-        kv = *(const float4*)(kg + a.mqk.row_off(key) + cc * 4);
-        vv = *(const float4*)(vg + a.mv.row_off(key) + cc * 4);
+        kv = *(const float4*)(kg + roff(a.mqk, key) + cc * 4);
+        vv = *(const float4*)(vg + roff(a.mv, key) + cc * 4);
       }
       *(float4*)(ks + r * D + cc * 4) = kv;
       *(float4*)(vs + r * D + cc * 4) = vv;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(Args a) {
   if (qok) {
     if (a.lse && part == 0) a.lse[(size_t)u * L + qi] = m_run + __log2f(l_run);
     const float inv = 1.f / l_run;
-    float* orow = og + a.mo.row_off(qi) + part * DL;
+    float* orow = og + roff(a.mo, qi) + part * DL;
 #pragma unroll
     for (int i = 0; i < DL; i += 4)
       *(float4*)(orow + i) = make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);

@@ -27,8 +27,9 @@ __global__ __launch_bounds__(256) void row_copy_kernel(CopyArgs a) {
     const uint32_t s = t - bh * a.U;
     const uint32_t b = a.fHeads.div(bh);
     const uint32_t h = bh - b * a.heads;
-    const int64_t so = a.ms.base(b, h, s) + a.ms.row_off(r);
-    const int64_t dso = a.md.base(b, h, s) + a.md.row_off(r);
+    const uint32_t ru = a.row_unit > 1 ? a.row_unit : 1u;
+    const int64_t so = a.ms.base(b, h, s) + (int64_t)row_elems_rt(a.ms.row_off(r), ru);
+    const int64_t dso = a.md.base(b, h, s) + (int64_t)row_elems_rt(a.md.row_off(r), ru);
     const uint4 x = *(const uint4*)((const char*)a.src + (so * a.elem_bytes) + (uint64_t)cc * 16);
     *(uint4*)((char*)a.dst + (dso * a.elem_bytes) + (uint64_t)cc * 16) = x;
   }

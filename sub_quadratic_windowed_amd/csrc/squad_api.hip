@@ -22,6 +22,7 @@ struct Geo {
   int64_t nt, nh, nw;           // window grid (cut tilings: rounded up)
   int64_t G, Wn, n;             // windows, tile cells per window, tokens
   bool cut;                     // the grid is not a whole number of tiles
+  uint32_t ru = 1;              // row unit of the maps: 1 (narrow) or head_dim (wide)
 };
 
 // cut: whether the entry point accepts grids that are not a whole number of tiles
@@ -69,15 +70,18 @@ Mix mix(uint32_t x1, uint32_t x0, int64_t s2, int64_t s1, int64_t s0) {
 
 Mix linear(int64_t stride) { return mix(1, 1, stride, 0, 0); }
 
-Mix32 mix32(uint32_t x1, uint32_t x0, int64_t s2, int64_t s1, int64_t s0) {
+// ru: the row unit (strides in elements are divided by it; every stride is a
+// multiple of head_dim, so wide maps hold whole head rows).  The strides are kept
+// modulo 2^32: every row offset formed from them is below 2^32.
+Mix32 mix32(uint32_t x1, uint32_t x0, int64_t s2, int64_t s1, int64_t s0, int64_t ru = 1) {
   Mix32 m;
   m.x1 = FastDiv32(x1);
   m.x0 = FastDiv32(x0);
-  m.s2 = (int32_t)s2; m.s1 = (int32_t)s1; m.s0 = (int32_t)s0;
+  m.s2 = (int32_t)(uint32_t)(s2 / ru); m.s1 = (int32_t)(uint32_t)(s1 / ru); m.s0 = (int32_t)(uint32_t)(s0 / ru);
   return m;
 }
 
-Mix32 linear32(int64_t stride) { return mix32(1, 1, stride, 0, 0); }
+Mix32 linear32(int64_t stride, int64_t ru = 1) { return mix32(1, 1, stride, 0, 0, ru); }
 
 // Token order [B, n, heads, d]: the window part and the offset part of a token index.
 // (nh, nw, strides) of the window digits and (th, tw, strides) of the offset digits.
@@ -92,10 +96,10 @@ RowMap token_map(const Geo& g, int64_t heads, int64_t d, bool by_window, int64_t
   const int64_t o2 = g.H * g.W * ts, o1 = g.W * ts, o0 = ts;
   if (by_window) {
     m.unit = mix((uint32_t)g.nh, (uint32_t)g.nw, w2, w1, w0);
-    m.row = mix32((uint32_t)g.th, (uint32_t)g.tw, o2, o1, o0);
+    m.row = mix32((uint32_t)g.th, (uint32_t)g.tw, o2, o1, o0, g.ru);
   } else {
     m.unit = mix((uint32_t)g.th, (uint32_t)g.tw, o2, o1, o0);
-    m.row = mix32((uint32_t)g.nh, (uint32_t)g.nw, w2, w1, w0);
+    m.row = mix32((uint32_t)g.nh, (uint32_t)g.nw, w2, w1, w0, g.ru);
   }
   return m;
 }
@@ -106,7 +110,7 @@ RowMap group_major_map(const Geo& g, int64_t heads, int64_t d, bool by_window) {
   m.sB = heads * g.Wn * g.G * d;
   m.sH = g.Wn * g.G * d;
   m.unit = by_window ? linear(d) : linear(g.G * d);
-  m.row = by_window ? linear32(g.G * d) : linear32(d);
+  m.row = by_window ? linear32(g.G * d, g.ru) : linear32(d, g.ru);
   return m;
 }
 
@@ -116,7 +120,7 @@ RowMap window_major_map(const Geo& g, int64_t heads, int64_t d, bool by_window) 
   m.sB = heads * g.G * g.Wn * d;
   m.sH = g.G * g.Wn * d;
   m.unit = by_window ? linear(g.Wn * d) : linear(d);
-  m.row = by_window ? linear32(d) : linear32(g.Wn * d);
+  m.row = by_window ? linear32(d, g.ru) : linear32(g.Wn * d, g.ru);
   return m;
 }
 
@@ -131,6 +135,7 @@ AttnArgs attn_args(const void* q, const void* k, const void* v, void* o, uint32_
   a.units = a.BH * U;
   const double s = scale > 0.f ? (double)scale : 1.0 / sqrt((double)head_dim);
   a.c = (float)(s * 1.4426950408889634);  // log2(e)
+  a.row_unit = 1;
   return a;
 }
 
@@ -141,6 +146,19 @@ int run_attn(AttnArgs a, int32_t head_dim, int32_t dtype, hipStream_t stream,
   const hipError_t e = dtype == SQUAD_DTYPE_BF16 ? launch_attn_bf16(a, head_dim, vtype, stream)
                                                  : launch_attn_f32(a, head_dim, stream);
   return e == hipSuccess ? SQUAD_OK : SQUAD_ERR_HIP;
+}
+
+// The row unit for tensors of `span` elements per batch element (every row offset of
+// a call's maps is below it): narrow below 2^31 elements, else wide, up to 2^32 - 1
+// head rows.
+int pick_row_unit(Geo& g, uint64_t span, int32_t head_dim) {
+  if (span < (uint64_t(1) << 31)) {
+    g.ru = 1;
+    return SQUAD_OK;
+  }
+  if ((span + head_dim - 1) / head_dim >= (uint64_t)kNoRow) return SQUAD_ERR_SHAPE;
+  g.ru = (uint32_t)head_dim;
+  return SQUAD_OK;
 }
 
 bool too_many_units(uint64_t bh, uint64_t units_per_bh, uint64_t rows) {
@@ -160,8 +178,10 @@ int check_grid_call(const int32_t grid[3], const int32_t tile[3], int32_t heads,
   const uint64_t bh = (uint64_t)heads * (uint64_t)batch;
   const uint64_t cells = (uint64_t)g.G * (uint64_t)g.Wn;
   if (too_many_units(bh, (uint64_t)(g.G > g.Wn ? g.G : g.Wn), bh * cells)) return SQUAD_ERR_SHAPE;
-  // the kernels address rows inside one batch element with 32-bit offsets
-  if (cells * (uint64_t)heads * (uint64_t)head_dim >= (uint64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  // rows inside one batch element are located by 32-bit offsets: in elements while
+  // they stay below 2^31 (narrow maps), else in head rows (wide maps)
+  st = pick_row_unit(g, cells * (uint64_t)heads * (uint64_t)head_dim, head_dim);
+  if (st) return st;
   bytes = (size_t)bh * (size_t)g.n * (size_t)head_dim * elem_bytes(dtype);
   if (wbytes) *wbytes = (size_t)bh * (size_t)cells * (size_t)head_dim * elem_bytes(dtype);
   return SQUAD_OK;
@@ -180,10 +200,11 @@ int check_ptrs(const void* const* in, int nin, const void* out, size_t bytes) {
 }
 
 int run_copy(const void* src, void* dst, const RowMap& ms, const RowMap& md, uint32_t L, uint32_t U,
-             uint32_t heads, uint32_t batch, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+             uint32_t heads, uint32_t batch, int32_t head_dim, int32_t dtype, uint32_t ru, hipStream_t stream) {
   CopyArgs c;
   memset(&c, 0, sizeof(c));
   c.src = src; c.dst = dst; c.ms = ms; c.md = md;
+  c.row_unit = ru;
   c.L = L; c.U = U; c.heads = heads; c.BH = heads * batch;
   c.fL = FastDiv(L); c.fU = FastDiv(U); c.fHeads = FastDiv(heads);
   c.rows = c.BH * U * L;
@@ -257,9 +278,12 @@ int check_forward(const void* const* in, int nin, const void* out, const int32_t
 // Cut tilings: a row is present iff its token lies inside the grid.  Token
 // coordinate on each axis = window digit * tile size + offset digit; the local
 // pass's units are windows (rows offsets), the global pass's the reverse.
+// Wide maps are served by the kernels' cut form only: they are marked cut on whole
+// tilings too (where every row is present).  Sets the row unit of the maps.
 template <typename Args>
 void set_cut(Args& a, const Geo& g, bool by_window) {
-  if (!g.cut) return;
+  a.row_unit = g.ru;
+  if (!g.cut && g.ru == 1) return;
   a.cut.on = 1;
   a.cut.lim[0] = (uint32_t)g.T; a.cut.lim[1] = (uint32_t)g.H; a.cut.lim[2] = (uint32_t)g.W;
   const uint32_t tl[3] = {(uint32_t)g.tt, (uint32_t)g.th, (uint32_t)g.tw};
@@ -501,7 +525,7 @@ int squad_tile_gather(const void* src, void* dst, const int32_t grid[3], const i
   st = check_ptrs(in, 1, dst, bytes);
   if (st) return st;
   return run_copy(src, dst, token_map(g, heads, head_dim, true), window_major_map(g, heads, head_dim, true),
-                  (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, dtype, (hipStream_t)stream);
+                  (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, dtype, g.ru, (hipStream_t)stream);
 }
 
 int squad_tile_scatter(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
@@ -515,7 +539,7 @@ int squad_tile_scatter(const void* src, void* dst, const int32_t grid[3], const 
   st = check_ptrs(in, 1, dst, bytes);
   if (st) return st;
   return run_copy(src, dst, window_major_map(g, heads, head_dim, true), token_map(g, heads, head_dim, true),
-                  (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, dtype, (hipStream_t)stream);
+                  (uint32_t)g.Wn, (uint32_t)g.G, heads, batch, head_dim, dtype, g.ru, (hipStream_t)stream);
 }
 
 int squad_window_to_group(const void* src, void* dst, const int32_t grid[3], const int32_t tile[3],
@@ -530,7 +554,7 @@ int squad_window_to_group(const void* src, void* dst, const int32_t grid[3], con
   if (st) return st;
   // enumerate rows in the group-major (destination) order: units = offsets, rows = windows
   return run_copy(src, dst, window_major_map(g, heads, head_dim, false), group_major_map(g, heads, head_dim, false),
-                  (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, dtype, (hipStream_t)stream);
+                  (uint32_t)g.G, (uint32_t)g.Wn, heads, batch, head_dim, dtype, g.ru, (hipStream_t)stream);
 }
 
 int squad_window_attn(const void* q, const void* k, const void* v, void* out, int32_t units,
@@ -658,7 +682,8 @@ int squad_debug_row_offsets(int32_t which, const int32_t grid[3], const int32_t 
         const int64_t base = m.base(b, h, s);
         const UnitDigits ud = cut_unit_digits(a, s);
         for (uint32_t r = 0; r < L; ++r)
-          offsets[i++] = (!a.cut.on || cut_present(a, ud, r)) ? base + m.row_off(r) : -1;
+          offsets[i++] = (!a.cut.on || cut_present(a, ud, r)) ? base + (int64_t)row_elems_rt(m.row_off(r), g.ru)
+                                                                : -1;
       }
   return SQUAD_OK;
 }
@@ -752,7 +777,7 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   // the global pass's key side (bf16, when it runs as the two kinds) also leaves D
   // of the local pass, <do1, o1>, for the rows of every window; the local pass's
   // query side then reads it instead of the local output
-  const bool hand_off = bf16 && !bwd_bf16_fused(ag.L, ag.cut.on) && !bwd_bf16_fused(g.Wn, g.cut);
+  const bool hand_off = bf16 && !bwd_bf16_fused(ag.L, ag.cut.on) && !bwd_bf16_fused(g.Wn, g.cut || g.ru > 1);
   if (hand_off) ag.dsum_next = (float*)(ws + t.dsum_l);
   st = run_bwd(ag, head_dim, dtype, BwdTypes{true, false}, s);
   if (st) return st;
@@ -1118,6 +1143,14 @@ int block_layout(const Geo& g, int32_t heads, int32_t batch, int32_t head_dim, i
   return SQUAD_OK;
 }
 
+// q, k, v of the block are slices of the projection's rows (stride 3 * hidden):
+// the maps' row unit covers that span too.
+int block_row_unit(Geo& g, int32_t heads, int32_t head_dim) {
+  const uint64_t hidden = (uint64_t)heads * (uint64_t)head_dim;
+  const uint64_t cells = (uint64_t)g.G * (uint64_t)g.Wn;
+  return pick_row_unit(g, std::max(cells * hidden, (uint64_t)g.n * 3 * hidden), head_dim);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1142,7 +1175,7 @@ size_t squad_block_workspace_size(const int32_t grid[3], const int32_t tile[3], 
   if (check_grid_call(grid, tile, heads, batch, head_dim, dtype, g, bytes, nullptr, true)) return 0;
   BlockLayout b;
   if (block_layout(g, heads, batch, head_dim, dtype, b)) return 0;
-  if (g.n * 3 * (int64_t)heads * head_dim >= (int64_t(1) << 31)) return 0;   // as squad_block_forward
+  if (block_row_unit(g, heads, head_dim)) return 0;   // as squad_block_forward
   return b.total;
 }
 
@@ -1159,8 +1192,10 @@ int squad_block_forward(const void* x, const void* w_qkv, const void* w_out, con
   st = block_layout(g, heads, batch, head_dim, dtype, lay);
   if (st) return st;
   const int64_t hidden = (int64_t)heads * head_dim;
-  // the attention addresses q, k, v rows (stride 3 * hidden) with 32-bit offsets
-  if (g.n * 3 * hidden >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
+  st = block_row_unit(g, heads, head_dim);
+  if (st) return st;
+  // the dense comparator takes narrow maps only
+  if (dense && g.ru > 1) return SQUAD_ERR_SHAPE;
   if ((int64_t)batch * g.n >= (int64_t(1) << 31) || 3 * hidden >= (int64_t(1) << 31)) return SQUAD_ERR_SHAPE;
   const size_t wq_bytes = (size_t)3 * hidden * hidden * elem_bytes(dtype);
   const size_t wo_bytes = (size_t)hidden * hidden * elem_bytes(dtype);

@@ -45,6 +45,7 @@ struct AttnArgsT {
   float c;           // softmax scale * log2(e)
   Cut cut;           // absent rows (cut tilings only; on == 0 otherwise)
   float* lse;        // optional: row statistics lse[u * L + r] = log2 sum_j exp2(c <q_r, k_j>)
+  uint32_t row_unit; // elements per unit of the maps' row offsets: 1 (narrow), head_dim (wide)
 };
 typedef AttnArgsT<RowMap> AttnArgs;
 typedef AttnArgsT<RowMapK> AttnArgsK;   // six-digit units (middle passes of k levels)
@@ -119,6 +120,7 @@ struct BwdArgsT {
   float c;            // softmax scale * log2(e)
   float scale;
   Cut cut;
+  uint32_t row_unit;  // elements per unit of the maps' row offsets: 1 (narrow), head_dim (wide)
 };
 typedef BwdArgsT<RowMap> BwdArgs;
 typedef BwdArgsT<RowMapK> BwdArgsK;   // middle levels of a k-level operator
@@ -150,12 +152,13 @@ hipError_t launch_bwd_bf16_small_k(BwdArgsK a, int head_dim, hipStream_t stream)
 struct CopyArgs {
   const void* src;
   void* dst;
-  RowMap ms, md;      // offsets in elements
+  RowMap ms, md;      // offsets in elements (rows: in units of row_unit elements)
   uint32_t L, U, heads, BH;
   FastDiv fL, fU, fHeads;
   uint32_t rows;      // BH * U * L
   uint32_t row_chunks_log2;  // log2 of the 16-byte chunks per row
   uint32_t elem_bytes;  // 2 or 4
+  uint32_t row_unit;  // 1 (narrow maps) or head_dim (wide maps)
 };
 
 hipError_t launch_row_copy(CopyArgs a, hipStream_t stream);

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace squad {
 
 // Division by a runtime constant d >= 1 for dividends x < 2^32:
@@ -100,7 +102,8 @@ struct Mix {
 };
 
 // Row part of a map: evaluated per key block in the attention loop, 32-bit (the
-// host guarantees every row offset inside one (batch, head) is below 2^31).
+// host guarantees every row offset inside one (batch, head) is below 2^31 elements,
+// or, for wide maps, below 2^32 - 1 head rows; see kNoRow).
 struct Mix32 {
   FastDiv32 x1, x0;
   int32_t s2, s1, s0;
@@ -125,6 +128,35 @@ struct Mix32 {
 // and zero-extended where it is added to a pointer (doubling a signed offset would
 // turn offsets of 2^30 elements and more negative).
 __host__ __device__ __forceinline__ uint32_t bytes16(int32_t e) { return 2u * (uint32_t)e; }
+
+// Narrow and wide row maps.  A narrow map (the default) holds row offsets in
+// elements, below 2^31.  A wide map holds them in units of one head row (head_dim
+// elements: every row stride of every map is a multiple of head_dim), below
+// 2^32 - 1, for tensors whose rows inside one batch element span 2^31 elements
+// or more (up to 2^32 - 1 head rows).  The unit part of a map is in elements either
+// way (64-bit).  The all-ones offset never occurs, so it can mark an absent row.
+constexpr uint32_t kNoRow = 0xffffffffu;
+
+// Element offset of a row of a map with D-element head rows (narrow: the offset
+// itself, non-negative, so it is added zero-extended).
+template <bool WIDE, int D>
+__host__ __device__ __forceinline__ typename std::conditional<WIDE, uint64_t, uint32_t>::type row_elems(int32_t e) {
+  if constexpr (WIDE) return (uint64_t)(uint32_t)e * (uint64_t)D;
+  else return (uint32_t)e;
+}
+// Byte offset of a row of a 16-bit tensor: narrow maps give an unsigned 32-bit
+// offset (exact below 2^32 bytes; added zero-extended, so that the loads keep a
+// uniform 64-bit base and one 32-bit offset register), wide maps a 64-bit one.
+template <bool WIDE, int D>
+__host__ __device__ __forceinline__ typename std::conditional<WIDE, uint64_t, uint32_t>::type row_bytes16(int32_t e) {
+  if constexpr (WIDE) return (uint64_t)(uint32_t)e * (uint64_t)(2 * D);
+  else return bytes16(e);
+}
+// The same at run time (engines whose kernels are not specialised on the width):
+// `unit` is 1 for narrow maps and head_dim for wide ones.
+__host__ __device__ __forceinline__ uint64_t row_elems_rt(int32_t e, uint32_t unit) {
+  return (uint64_t)(uint32_t)e * unit;
+}
 
 struct RowMap {
   int64_t sB, sH; // batch and head strides (elements)

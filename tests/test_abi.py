@@ -178,6 +178,54 @@ def test_row_maps_at_full_size():
     assert np.array_equal(got0[5], (idx * heads + 5) * 128)
 
 
+def test_wide_row_maps_past_2_to_the_31():
+    """Tensors of 2^31 elements or more per batch element take wide maps (row offsets
+    in head rows): 128^3 tokens x 8 heads x 128 dims = 2^31.  The offsets the maps
+    give, turned back into elements, are every row of each tensor exactly once, and
+    the local pass's token map puts head h of window g, offset p at the oracle's
+    token index (g, p)."""
+    grid, tile, heads, d = (128, 128, 128), (8, 16, 16), 8, 128
+    n = 128 ** 3
+    assert n * heads * d == 1 << 31
+    idx = oracle.window_index(grid, tile)             # [G, Wn] token indices
+    got0 = sq.squad_debug_row_offsets(0, grid, tile, heads, 1, d)
+    assert np.array_equal(np.sort(got0), np.arange(n * heads, dtype=np.int64) * d)
+    got0 = got0.reshape(heads, *idx.shape)
+    for h in (0, 5, 7):
+        assert np.array_equal(got0[h], (idx.astype(np.int64) * heads + h) * d)
+    del got0
+    got1 = sq.squad_debug_row_offsets(1, grid, tile, heads, 1, d).reshape(heads, idx.shape[1], idx.shape[0])
+    assert np.array_equal(got1[7], (idx.T.astype(np.int64) * heads + 7) * d)
+    del got1
+    for which in (2, 3):   # the workspace, group-major
+        got = sq.squad_debug_row_offsets(which, grid, tile, heads, 1, d)
+        assert np.array_equal(np.sort(got), np.arange(n * heads, dtype=np.int64) * d)
+
+
+def test_wide_row_maps_on_a_cut_tiling():
+    """A cut tiling past 2^31 elements (127 x 128 x 130 grid, 8 x 16 x 16 tiles:
+    1,152 windows of 2,048 cells, 2,113,280 tokens, 8 heads x 128): the present
+    rows of both token maps are every row of the tensor once; absent rows read -1."""
+    grid, tile, heads, d = (127, 128, 130), (8, 16, 16), 8, 128
+    n = 127 * 128 * 130
+    cells = 16 * 8 * 9 * 2048
+    assert cells * heads * d >= 1 << 31
+    for which in (0, 1):
+        got = sq.squad_debug_row_offsets(which, grid, tile, heads, 1, d)
+        assert got.size == cells * heads
+        present = got[got >= 0]
+        assert (got == -1).sum() == (cells - n) * heads
+        assert np.array_equal(np.sort(present), np.arange(n * heads, dtype=np.int64) * d)
+
+
+def test_row_unit_limits():
+    """Wide maps reach 2^32 - 2 head rows per batch element: 2^30 cells x 3 heads
+    are accepted (workspace size above zero), x 4 heads (2^32 rows) are not."""
+    g, t = (1024, 1024, 1024), (16, 32, 32)
+    assert sq.squad_attn_workspace_size(g, t, 3, 1, 128, 1) == 3 * (1 << 30) * 128 * 2
+    assert sq.squad_attn_workspace_size(g, t, 4, 1, 128, 1) == 0
+
+
 def _device_count():
     try:
         import torch
@@ -411,10 +459,10 @@ def test_block_entry_point_rejects_bad_arguments():
     assert blk(ws=0) == WORKSPACE
     assert blk(wb=need - 1) == WORKSPACE
     assert blk(y=Y + 8) == ALIGN
-    # q, k, v rows at a stride of 3 hidden must keep 32-bit in-unit offsets:
-    # 245,760 tokens x 3 x 3072 passes 2^31
-    assert blk(grid=_lib.int3((64, 48, 80)), d=128, heads=24, wb=1 << 40) == SHAPE
-    assert sq.squad_block_workspace_size((64, 48, 80), (4, 12, 10), 24, 1, 128, 1) == 0
+    # q, k, v rows at a stride of 3 hidden: 245,760 tokens x 3 x 3072 passes 2^31
+    # elements, so the block's maps are wide; the dense comparator takes narrow maps only
+    assert blk(grid=_lib.int3((64, 48, 80)), d=128, heads=24, dense=1, wb=1 << 40) == SHAPE
+    assert sq.squad_block_workspace_size((64, 48, 80), (4, 12, 10), 24, 1, 128, 1) > 0
     assert sq.squad_block_workspace_size((32, 24, 40), (2, 8, 10), 24, 1, 128, 1) > 0
 
 
