@@ -44,6 +44,13 @@
  * 65504 or more overflow there and surface as inf/nan in the output.
  * head_dim must be 64 or 128.
  * scale <= 0 selects the softmax scale 1/sqrt(head_dim).
+ * Sizes: G * Wn (tile cells, absent ones included) below 2^31, and per batch
+ * element G * Wn * heads below 2^32 - 1 head rows (a bf16 tensor of up to 2^39
+ * bytes at head_dim 128); SQUAD_ERR_SHAPE beyond.  Rows of tensors below 2^31
+ * elements per batch element are located with 32-bit element offsets; larger
+ * ones with offsets in head rows and 64-bit addresses (the 16-bit engine then
+ * takes its table-free, per-block presence form).  The k-level entry points
+ * keep the first limit: n * heads * head_dim below 2^31.
  *
  * Pointers are device pointers that the caller owns; base pointers must be 16-byte
  * aligned.  The library never allocates or frees device memory and never
@@ -237,7 +244,8 @@ int squad_plan_tile(const int32_t grid[3], int32_t tile_out[3]);
  * from the projection's output rows (row stride 3 hidden).  `workspace` holds qkv,
  * the operator's workspace and a (squad_block_workspace_size bytes).  Statuses as
  * for squad_attn_forward (SQUAD_ERR_INVALID_ARG for a null handle), plus
- * SQUAD_ERR_SHAPE when n * 3 * hidden reaches 2^31.  The call keeps no state of
+ * SQUAD_ERR_SHAPE if dense = 1 and n * 3 * hidden reaches 2^31 (the comparator
+ * keeps 32-bit element offsets).  The call keeps no state of
  * its own; rocBLAS may allocate device memory on the handle, which the handle owns.
  *
  * squad_blas_create: a rocBLAS handle on the current device for squad_block_forward
