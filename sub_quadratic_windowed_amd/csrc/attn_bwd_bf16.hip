@@ -47,6 +47,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -219,22 +220,40 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Store a transposed accumulator tile set: lane l32 (and l32 + 32) owns row l32,
 // holding its element dim 32 mt + 8 (r / 4) + 4 half + r % 4 in acc[mt][r]; `off` is
 // the row's offset under the map (kNoRow: not stored).  Each value is scaled, then
-// written as fp32 (kAccWrite), added to the fp32 accumulator and written back
-// (kAccAdd), or added to it and written as bf16 to outp (kAccFinal; with no
-// accumulator, plainly written).  The rows pass through `stage` (32 rows x D / 2
-// fp32 = 64 D bytes of LDS, the wave's own) half a row at a time and go out as
-// whole row segments, 16 bytes per lane, so a store instruction covers 64 / (D / 8)
-// rows' contiguous bytes rather than 16-byte pieces of 32 rows.  Chunks are
+// - kAccWrite: written as fp32 to accp; kAccAdd: added to the fp32 accumulator and
+//   written back; kAccFinal: added to it (if any) and written as bf16 to outp;
+// - kPartWrite: written to outp as fp16 times a power of two 2^e per row, e chosen
+//   so that the row's largest magnitude lies in [2^14, 2^15) (e clamped to
+//   [-126, 126]), with 2^-e stored at scp[row]; kPartFinal: outp holds such a
+//   part, which is added (times scp[row]) before the sum is written as bf16 to outp.
+// scp is indexed by the row's element offset / D (the scale array has one float
+// per head row of the tensor).  The rows pass through `stage` (32 rows x D / 2 fp32 =
+// 64 D bytes of LDS, the wave's own) half a row at a time and go out as whole row
+// segments, 16 (fp32) or 8 (16-bit) bytes per lane, so a store instruction covers
+// 64 / (D / 8) rows' contiguous bytes rather than pieces of 32 rows.  Chunks are
 // XOR-swizzled by row in LDS.
 template <int D, bool WIDE = false>
 __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], float scale, uint32_t lane,
                                                uint32_t mode, float* accp, __bf16* outp, uint32_t off,
-                                               char* stage) {
+                                               char* stage, float* scp = nullptr) {
   constexpr int DR = D / 2;        // fp32 dims per round
   constexpr int NCH = DR / 4;      // 16-byte chunks per staged row
   constexpr int MTR = D / 64;      // accumulator tiles per round
   constexpr int RPI = 64 / NCH;    // rows per store instruction
   const uint32_t half = lane >> 5, l32 = lane & 31;
+  const bool part = mode == kPartWrite || mode == kPartFinal;
+  // kPartWrite: this row's exponent e (lanes l32 and l32 + 32 agree)
+  int32_t e_row = 0;
+  if (mode == kPartWrite) {
+    float amax = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[mt][r] * scale));
+    amax = max_halves(amax);
+    // amax = f 2^k, f in [0.5, 1): amax 2^(15 - k) = f 2^15 lies in [2^14, 2^15)
+    e_row = min(max(15 - __builtin_amdgcn_frexp_expf(amax), -126), 126);
+  }
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
 #pragma unroll
@@ -253,10 +272,30 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], floa
     for (int i = 0; i < 32 / RPI; ++i) {
       const uint32_t r = i * RPI + lane / NCH;
       const uint32_t o = (uint32_t)__shfl((int)off, (int)r, 64);
+      const int32_t er = __shfl(e_row, (int)r, 64);
       float4 x = *(const float4*)(stage + r * (DR * 4) + ((c ^ (r & (NCH - 1))) << 4));
       if (o != kNoRow) {
         const auto oe = row_elems<WIDE, D>((int32_t)o);
         const int d0 = DR * rd + 4 * c;
+        if (part) {
+          float* sp = scp + oe / D;
+          if (mode == kPartWrite) {
+            const float up = __builtin_amdgcn_ldexpf(1.f, er);
+            f16x4 w;
+            w[0] = (_Float16)(x.x * up); w[1] = (_Float16)(x.y * up);
+            w[2] = (_Float16)(x.z * up); w[3] = (_Float16)(x.w * up);
+            *(f16x4*)((_Float16*)outp + oe + d0) = w;
+            if (rd == 0 && c == 0) *sp = __builtin_amdgcn_ldexpf(1.f, -er);
+          } else {
+            const float down = *sp;
+            const f16x4 y = *(const f16x4*)((const _Float16*)outp + oe + d0);
+            bf16x4 w;
+            w[0] = (__bf16)fmaf((float)y[0], down, x.x); w[1] = (__bf16)fmaf((float)y[1], down, x.y);
+            w[2] = (__bf16)fmaf((float)y[2], down, x.z); w[3] = (__bf16)fmaf((float)y[3], down, x.w);
+            *(bf16x4*)(outp + oe + d0) = w;
+          }
+          continue;
+        }
         if (mode != kAccWrite && accp) {
           const float4 y = *(const float4*)(accp + oe + d0);
           x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
@@ -484,9 +523,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
              : wave == 1 ? BStage<D, 1, 0>::ptr()
              : wave == 2 ? BStage<D, 2, 0>::ptr() : BStage<D, 0, 1>::ptr();
     const int64_t base = a.mdq.base(p.b, p.h, p.s);
-    store_rows_lds<D, WIDE>(acc, a.scale, lane, a.final_pass, a.dq_acc + base,
-                      a.final_pass == kAccFinal ? (__bf16*)a.dq + base : nullptr,
-                      qok ? (uint32_t)a.mdq.row_off(qi) : kNoRow, st);
+    store_rows_lds<D, WIDE>(acc, a.scale, lane, a.final_pass, a.dq_acc ? a.dq_acc + base : nullptr,
+                            a.final_pass != kAccWrite && a.final_pass != kAccAdd ? (__bf16*)a.dq + base : nullptr,
+                            qok ? (uint32_t)a.mdq.row_off(qi) : kNoRow, st, a.dq_sc ? a.dq_sc + base / D : nullptr);
   }
 }
 
@@ -698,9 +737,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   if (active) {
     char* st = (char*)vown + wave * 32 * D * 2;
     const int64_t kbase = a.mdk.base(p.b, p.h, p.s), vbase = a.mdv.base(p.b, p.h, p.s);
-    store_rows_lds<D, WIDE>(dka, a.scale, lane, a.final_pass, a.dk_acc + kbase,
-                      a.final_pass == kAccFinal ? (__bf16*)a.dk + kbase : nullptr,
-                      kok ? (uint32_t)a.mdk.row_off(kj) : kNoRow, st);
+    store_rows_lds<D, WIDE>(dka, a.scale, lane, a.final_pass, a.dk_acc ? a.dk_acc + kbase : nullptr,
+                            a.final_pass != kAccWrite && a.final_pass != kAccAdd ? (__bf16*)a.dk + kbase : nullptr,
+                      kok ? (uint32_t)a.mdk.row_off(kj) : kNoRow, st, a.dk_sc ? a.dk_sc + kbase / D : nullptr);
     store_rows_lds<D, WIDE>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vbase,
                       kok ? (uint32_t)a.mdv.row_off(kj) : kNoRow, st);
   }
@@ -861,9 +900,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
       if (nb > 1) ds1[q * PITCH + rj] = rok ? sbk[1][r / 8][r % 8] : (__bf16)0.f;
     }
     const int64_t kb0 = a.mdk.base(p.b, p.h, p.s), vb0 = a.mdv.base(p.b, p.h, p.s);
-    store_rows_lds<D>(dka, a.scale, lane, a.final_pass, a.dk_acc + kb0,
-                      a.final_pass == kAccFinal ? (__bf16*)a.dk + kb0 : nullptr,
-                      rok ? (uint32_t)a.mdk.row_off(rj) : kNoRow, own_stage);
+    store_rows_lds<D>(dka, a.scale, lane, a.final_pass, a.dk_acc ? a.dk_acc + kb0 : nullptr,
+                      a.final_pass != kAccWrite && a.final_pass != kAccAdd ? (__bf16*)a.dk + kb0 : nullptr,
+                      rok ? (uint32_t)a.mdk.row_off(rj) : kNoRow, own_stage,
+                      a.dk_sc ? a.dk_sc + kb0 / D : nullptr);
     store_rows_lds<D>(dva, 1.f, lane, kAccFinal, nullptr, (__bf16*)a.dv + vb0,
                       rok ? (uint32_t)a.mdv.row_off(rj) : kNoRow, own_stage);
   }
@@ -895,9 +935,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2))) void b
   dq_block(0, std::integral_constant<int, 0>{});
   if (nb > 1) dq_block(1, std::integral_constant<int, 1>{});
   const int64_t qb0 = a.mdq.base(p.b, p.h, p.s);
-  store_rows_lds<D>(acc, a.scale, lane, a.final_pass, a.dq_acc + qb0,
-                    a.final_pass == kAccFinal ? (__bf16*)a.dq + qb0 : nullptr,
-                    rok ? (uint32_t)a.mdq.row_off(rj) : kNoRow, own_stage);
+  store_rows_lds<D>(acc, a.scale, lane, a.final_pass, a.dq_acc ? a.dq_acc + qb0 : nullptr,
+                    a.final_pass != kAccWrite && a.final_pass != kAccAdd ? (__bf16*)a.dq + qb0 : nullptr,
+                    rok ? (uint32_t)a.mdq.row_off(rj) : kNoRow, own_stage, a.dq_sc ? a.dq_sc + qb0 / D : nullptr);
 }
 
 template <int D, int NW, bool VF16, bool OF16, typename Args>

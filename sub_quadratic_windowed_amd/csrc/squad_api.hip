@@ -326,7 +326,7 @@ int forward_global(const void* q, const void* k, void* out, const Geo& g, int32_
 // ---- training: the forward's saved state and the backward's scratch, in one
 // workspace (sections 256-byte aligned)
 struct TrainLayout {
-  size_t o1, lse_l, lse_g, dsum, dsum_l, do1, dq_acc, dk_acc, total;
+  size_t o1, lse_l, lse_g, dsum, dsum_l, do1, dq_sc, dk_sc, total;
 };
 
 TrainLayout train_layout(const Geo& g, int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
@@ -342,12 +342,14 @@ TrainLayout train_layout(const Geo& g, int32_t heads, int32_t batch, int32_t hea
   t.dsum_l = al(t.dsum + bh * cells * 4);
   t.do1 = al(t.dsum_l + bh * cells * 4);
   size_t end = al(t.do1 + bh * cells * head_dim * esz);
-  // bf16 calls sum dq and dk over the passes in fp32 (fp32 calls use dq and dk)
-  t.dq_acc = t.dk_acc = 0;
+  // bf16 calls hand the global pass's dq and dk parts to the local pass in dq and dk
+  // themselves, as scaled fp16 rows: one inverse scale per head row of each (fp32
+  // calls sum in dq and dk directly)
+  t.dq_sc = t.dk_sc = 0;
   if (dtype == SQUAD_DTYPE_BF16) {
-    t.dq_acc = end;
-    t.dk_acc = al(t.dq_acc + bh * (size_t)g.n * head_dim * 4);
-    end = al(t.dk_acc + bh * (size_t)g.n * head_dim * 4);
+    t.dq_sc = end;
+    t.dk_sc = al(t.dq_sc + bh * (size_t)g.n * 4);
+    end = al(t.dk_sc + bh * (size_t)g.n * 4);
   }
   t.total = end;
   return t;
@@ -758,8 +760,12 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dtype == SQUAD_DTYPE_BF16;
-  float* dq_acc = bf16 ? (float*)(ws + t.dq_acc) : (float*)dq;
-  float* dk_acc = bf16 ? (float*)(ws + t.dk_acc) : (float*)dk;
+  // fp32: dq and dk accumulate in place; bf16: the global pass's parts travel in dq
+  // and dk as scaled fp16 rows (2^-12 of the row's largest magnitude at most)
+  float* dq_acc = bf16 ? nullptr : (float*)dq;
+  float* dk_acc = bf16 ? nullptr : (float*)dk;
+  float* dq_sc = bf16 ? (float*)(ws + t.dq_sc) : nullptr;
+  float* dk_sc = bf16 ? (float*)(ws + t.dk_sc) : nullptr;
 
   // global pass: units = offset groups, values = the local output; its value
   // gradient (the local output's gradient) goes to the workspace, group-major
@@ -770,10 +776,10 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   ag.mo = ag.mqk; ag.mdo = ag.mqk;
   ag.lse = (const float*)(ws + t.lse_g);
   ag.dsum = (float*)(ws + t.dsum);
-  ag.dq_acc = dq_acc; ag.dk_acc = dk_acc;
+  ag.dq = dq; ag.dk = dk; ag.dq_acc = dq_acc; ag.dk_acc = dk_acc; ag.dq_sc = dq_sc; ag.dk_sc = dk_sc;
   ag.mdq = ag.mqk; ag.mdk = ag.mqk;
   ag.dv = ws + t.do1; ag.mdv = ag.mv;
-  ag.final_pass = 0;
+  ag.final_pass = bf16 ? kPartWrite : kAccWrite;
   // the global pass's key side (bf16, when it runs as the two kinds) also leaves D
   // of the local pass, <do1, o1>, for the rows of every window; the local pass's
   // query side then reads it instead of the local output
@@ -793,10 +799,10 @@ int squad_attn_backward(const void* q, const void* k, const void* v, const void*
   al.lse = (const float*)(ws + t.lse_l);
   al.dsum = (float*)(ws + (hand_off ? t.dsum_l : t.dsum));
   al.dsum_ready = hand_off ? 1 : 0;
-  al.dq = dq; al.dk = dk; al.dq_acc = dq_acc; al.dk_acc = dk_acc;
+  al.dq = dq; al.dk = dk; al.dq_acc = dq_acc; al.dk_acc = dk_acc; al.dq_sc = dq_sc; al.dk_sc = dk_sc;
   al.mdq = al.mqk; al.mdk = al.mqk;
   al.dv = dv; al.mdv = al.mqk;
-  al.final_pass = 1;
+  al.final_pass = bf16 ? kPartFinal : kAccFinal;
   return run_bwd(al, head_dim, dtype, BwdTypes{false, true}, s);
 }
 

@@ -86,12 +86,15 @@ hipError_t launch_attn_f32_k(AttnArgsK a, int head_dim, hipStream_t stream);
 //   kind A (per query row i):  D_i = <dout_i, o_i>;  dq_i = scale * sum_j dS_ij k_j
 //   kind B (per key row j):    dv_j = sum_i P_ij dout_i;  dk_j = scale * sum_i dS_ij q_i
 // with P_ij = exp2(c <q_i, k_j> - lse_i) and dS_ij = P_ij (<dout_i, v_j> - D_i).
-// Kind A writes D (dsum) for kind B.  dq and dk are summed over the passes: the
-// first pass writes its part to the fp32 accumulators (token order, the offsets
-// of mdq / mdk), middle passes (k levels) add to them, and the last adds them and
-// writes dq / dk in the call's dtype (for fp32 calls the accumulators may be dq
-// and dk themselves).
-enum BwdAcc : uint32_t { kAccWrite = 0, kAccFinal = 1, kAccAdd = 2 };
+// Kind A writes D (dsum) for kind B.  dq and dk are summed over the passes: with
+// k levels, the first pass writes its part to fp32 accumulators (token order, the
+// offsets of mdq / mdk), middle passes add to them, and the last adds them and
+// writes dq / dk in the call's dtype (for fp32 calls the accumulators are dq and dk
+// themselves).  The two-pass bf16 backward hands the global pass's dq and dk parts to the local
+// pass in the dq and dk buffers themselves, as fp16 rows scaled by a power of two
+// per row (the scale's inverse in dq_sc / dk_sc): kPartWrite writes them, kPartFinal
+// adds them and writes the bf16 gradients.
+enum BwdAcc : uint32_t { kAccWrite = 0, kAccFinal = 1, kAccAdd = 2, kPartWrite = 3, kPartFinal = 4 };
 template <typename Map>
 struct BwdArgsT {
   const void* q;
@@ -111,9 +114,11 @@ struct BwdArgsT {
   void* dk;           // kind B, final pass: dk
   float* dq_acc;      // fp32 accumulators (mdq / mdk offsets)
   float* dk_acc;
+  float* dq_sc;       // kPart modes: per head row of dq / dk, the inverse scale of its part
+  float* dk_sc;       // (index: the row's element offset / head_dim)
   void* dv;           // kind B: value gradient rows (mdv)
   Map mdq, mdk, mdv;
-  uint32_t final_pass;  // BwdAcc: write the accumulators / add them and write dq, dk / add to them
+  uint32_t final_pass;  // BwdAcc mode of the dq and dk stores
   uint32_t L, U, heads, BH;
   FastDiv fBH, fHeads;
   uint32_t units, nchunks;

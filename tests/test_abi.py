@@ -413,8 +413,9 @@ def test_training_entry_points_reject_bad_arguments():
     p = ctypes.c_void_p
     g, t = _lib.int3((4, 8, 8)), _lib.int3((1, 4, 4))
     need = sq.squad_attn_train_workspace_size((4, 8, 8), (1, 4, 4), 2, 1, 64, 1)
-    # O1 (fp16) + 3 per-row fp32 arrays + the local output's gradient + two fp32 accumulators
-    assert need >= 256 * 2 * 64 * 2 * 2 + 3 * 256 * 2 * 4 + 2 * 256 * 2 * 64 * 4
+    # O1 (fp16), 4 per-row fp32 arrays (two passes' statistics and D), the local
+    # output's gradient, and one inverse scale per head row of dq and of dk
+    assert need == 256 * 2 * 64 * 2 * 2 + 4 * 256 * 2 * 4 + 2 * 256 * 2 * 4
     assert sq.squad_attn_train_workspace_size((4, 8, 8), (5, 4, 4), 2, 1, 64, 1) == 0
     D, K, V, OUT, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
 
