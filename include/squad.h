@@ -50,7 +50,9 @@
  * elements per batch element are located with 32-bit element offsets; larger
  * ones with offsets in head rows and 64-bit addresses (the 16-bit engine then
  * takes its table-free, per-block presence form).  The k-level entry points
- * keep the first limit: n * heads * head_dim below 2^31.
+ * keep the first limit (n * heads * head_dim below 2^31), as do
+ * squad_window_attn (len * head_dim) and squad_dense_attn_forward
+ * (n * heads * head_dim).
  *
  * Pointers are device pointers that the caller owns; base pointers must be 16-byte
  * aligned.  The library never allocates or frees device memory and never
