@@ -184,7 +184,7 @@ int squad_attn_forward_noalloc(const void* q, const void* k, const void* v,
  * squad_attn_train_workspace_size: bytes of the one workspace both calls take
  * (the local output, each pass's per-row softmax statistic, and the backward's
  * scratch: the local output's gradient, per-row <dout, o>, and for bf16 calls
- * fp32 sums of dq and dk); 0 if the arguments are invalid.
+ * one scale per head row of dq and of dk); 0 if the arguments are invalid.
  *
  * squad_attn_forward_train: squad_attn_forward (same arguments and checks) that
  * also keeps, in `workspace`, what squad_attn_backward needs.  `out` is the same
@@ -197,7 +197,10 @@ int squad_attn_forward_noalloc(const void* q, const void* k, const void* v,
  * scratch part is overwritten).  bf16 calls compute in fp32 with bf16 MFMA
  * operands (P and dS rounded to bf16; the global pass's <dout, o1> products on
  * fp16 operands, dout scaled per row by a power of two) and round the gradients
- * to bf16 once.
+ * to bf16 once.  Between the passes, bf16 calls keep the global pass's dq and dk
+ * parts in dq and dk themselves, as fp16 rows scaled per row by a power of two
+ * (each element within 2^-12 of its row's largest magnitude); dq and dk are
+ * therefore written twice.
  * Statuses as for squad_attn_forward; the three outputs must not overlap each
  * other, an input or the workspace.  Work is enqueued on `stream`: four kernel
  * launches, no allocation, no synchronisation.
