@@ -898,7 +898,7 @@ int kpass_levels_forward(const void* q, const void* k, const void* v, const KGeo
 // two buffers for the intermediate outputs' gradients (the call's dtype), and for
 // bf16 calls the fp32 sums of dq and dk.
 struct KTrainLayout {
-  size_t inter, lse, dsum, dgrad[2], dq_acc, dk_acc, one_i, one_g, total;
+  size_t inter, lse, dsum, dgrad[2], dq_acc, dk_acc, dq_sc, dk_sc, one_i, one_g, total;
 };
 
 KTrainLayout kpass_train_layout(const KGeo& kg, int32_t heads, int32_t batch, int32_t head_dim, int32_t dtype) {
@@ -914,11 +914,18 @@ KTrainLayout kpass_train_layout(const KGeo& kg, int32_t heads, int32_t batch, in
   t.dgrad[0] = al(t.dsum + rows * 4);
   t.dgrad[1] = t.dgrad[0] + t.one_g;
   size_t end = t.dgrad[1] + t.one_g;
-  t.dq_acc = t.dk_acc = 0;
-  if (bf16) {
+  // bf16: with a middle level the dq and dk parts are summed in fp32 accumulators;
+  // with two levels the first level's parts travel in dq and dk as scaled fp16
+  // rows, as in squad_attn_backward (one inverse scale per head row)
+  t.dq_acc = t.dk_acc = t.dq_sc = t.dk_sc = 0;
+  if (bf16 && kg.k > 2) {
     t.dq_acc = end;
     t.dk_acc = al(t.dq_acc + rows * head_dim * 4);
     end = al(t.dk_acc + rows * head_dim * 4);
+  } else if (bf16) {
+    t.dq_sc = end;
+    t.dk_sc = al(t.dq_sc + rows * 4);
+    end = al(t.dk_sc + rows * 4);
   }
   t.total = end;
   return t;
@@ -1038,8 +1045,11 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dtype == SQUAD_DTYPE_BF16;
   const size_t rows = (size_t)heads * batch * kg.n;
-  float* dq_acc = bf16 ? (float*)(ws + t.dq_acc) : (float*)dq;
-  float* dk_acc = bf16 ? (float*)(ws + t.dk_acc) : (float*)dk;
+  const bool parts = bf16 && levels == 2;   // the fp16 part hand-off of two passes
+  float* dq_acc = parts ? nullptr : bf16 ? (float*)(ws + t.dq_acc) : (float*)dq;
+  float* dk_acc = parts ? nullptr : bf16 ? (float*)(ws + t.dk_acc) : (float*)dk;
+  float* dq_sc = parts ? (float*)(ws + t.dq_sc) : nullptr;
+  float* dk_sc = parts ? (float*)(ws + t.dk_sc) : nullptr;
   auto inter = [&](int j) -> void* { return ws + t.inter + (size_t)(j - 1) * t.one_i; };   // o_j, j >= 1
   // from the last level down: level j's values are o_j (v for j = 0), its output
   // o_(j+1) (out for the last), its upstream gradient that of o_(j+1) (dout for
@@ -1049,7 +1059,8 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
     const void* outj = j == levels - 1 ? out : inter(j + 1);
     const void* up = j == levels - 1 ? dout : ws + t.dgrad[(j + 1) & 1];
     void* dvj = j == 0 ? dv : ws + t.dgrad[j & 1];
-    const uint32_t mode = j == levels - 1 ? kAccWrite : (j == 0 ? kAccFinal : kAccAdd);
+    const uint32_t mode = parts ? (j == 1 ? kPartWrite : kPartFinal)
+                                : j == levels - 1 ? kAccWrite : (j == 0 ? kAccFinal : kAccAdd);
     auto fill = [&](auto& a) {
       kpass_bwd_common(a, kg, j, heads, batch, head_dim, scale);
       a.q = q; a.k = k; a.v = vals; a.o = outj; a.dout = up;
@@ -1057,6 +1068,7 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
       a.lse = (const float*)(ws + t.lse) + (size_t)j * rows;
       a.dsum = (float*)(ws + t.dsum);
       a.dq = dq; a.dk = dk; a.dq_acc = dq_acc; a.dk_acc = dk_acc; a.dv = dvj;
+      a.dq_sc = dq_sc; a.dk_sc = dk_sc;
       a.final_pass = mode;
     };
     if (j == 0 || j == levels - 1) {
