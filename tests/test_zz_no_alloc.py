@@ -83,6 +83,24 @@ def test_noalloc_at_the_high_resolution_shape():
     assert torch.equal(out2, want2)
 
 
+def test_noalloc_with_wide_maps():
+    """64^3 tokens x 64 heads x 128 = 2^31 elements: the maps are wide, and one head's
+    local output (262,144 cells x 256 B = 64 MiB) fills the scratch exactly, so the
+    call runs 64 slices of one head; the result equals the workspace forward's."""
+    grid, tile, Hh = (64, 64, 64), (4, 8, 8), 64
+    gen = torch.Generator(device="cuda").manual_seed(46)
+    q, k, v = (torch.randn((1, 64 ** 3, Hh, 128), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    assert 64 ** 3 * 128 * 2 == _lib.NOALLOC_SCRATCH_BYTES
+    say("noalloc: wide maps, 64 heads")
+    want = sq.squad_attn_forward(q, k, v, grid, tile, Hh)
+    out = sq.squad_attn_forward_noalloc(q, k, v, grid, tile, Hh)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+    del q, k, v, out, want
+    torch.cuda.empty_cache()
+
+
 def test_noalloc_rejects_a_head_past_the_scratch():
     grid, tile = (64, 64, 65), (4, 8, 5)   # 266,240 cells x 128 x 2 bytes > 64 MiB
     q = torch.zeros((1, 64 * 64 * 65, 1, 128), dtype=torch.bfloat16, device="cuda")
