@@ -165,3 +165,44 @@ def test_block_at_the_high_resolution_shape_equals_its_parts():
     assert torch.isfinite(y).all()
     assert float(diff.max()) <= 3e-2 * max(1.0, float(y2.float().abs().max()))
     assert float(diff.mean()) <= 2e-3
+
+
+@pytest.mark.timeout(600)
+def test_forward_with_wide_maps_head_dim_64_batch_2():
+    """head_dim 64 (the row unit is then 64 elements) and two batch elements, each
+    2^31 elements: 64^3 tokens x 128 heads x 64."""
+    Hh = 128
+    shape = (2, N, Hh, 64)
+    say(f"wide forward d64 {shape}")
+    q, k, v = (randn(shape, torch.bfloat16, 100 + i) for i in range(3))
+    out = sq.squad_attn_forward(q, k, v, GRID, TILE)
+    torch.cuda.synchronize()
+    hs = [0, Hh - 1]
+    want = oracle.squad_forward(f64(q[:, :, hs]), f64(k[:, :, hs]), f64(v[:, :, hs]), GRID, TILE)
+    got = f64(out[:, :, hs])
+    err = float(np.max(np.abs(got - want)))
+    say(f"  d64 batch 2 heads {hs}: max-abs {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= FWD_TOL[torch.bfloat16]
+
+
+@pytest.mark.timeout(900)
+def test_backward_with_wide_maps_on_a_cut_tiling():
+    grid = (63, 64, 65)
+    n = 63 * 64 * 65
+    shape = (1, n, HEADS, 128)
+    say(f"wide cut backward {shape}")
+    q, k, v, dout = (randn(shape, torch.bfloat16, 110 + i) for i in range(4))
+    out, ws = sq.squad_attn_forward_train(q, k, v, grid, TILE)
+    grads = sq.squad_attn_backward(q, k, v, out, dout, grid, TILE, ws)
+    torch.cuda.synchronize()
+    del ws
+    hs = [0, HEADS - 1]
+    want = oracle.squad_backward(*(f64(x[:, :, hs]) for x in (q, k, v, dout)), grid, TILE)
+    for name, g, w in zip(("dq", "dk", "dv"), grads, want):
+        g = f64(g[:, :, hs])
+        e = float(np.max(np.abs(g - w)))
+        ref = max(1.0, float(np.max(np.abs(w))))
+        say(f"  cut {name}: max-abs {e:.3e} (ref max {ref:.3f})")
+        assert np.isfinite(g).all()
+        assert e <= GRAD_TOL * ref, (name, e)
