@@ -323,6 +323,14 @@ def main():
     if not args.no_dense:
         block = block_rates(sq, inputs, dev)
 
+    graphs = None
+    if not args.no_dense:
+        print("[bench] graph replays of the small configurations", file=sys.stderr, flush=True)
+        try:
+            graphs = graph_rates(sq, inputs, dev)
+        except Exception as e:   # reported, not fatal: the headline line still prints
+            graphs = {"error": f"{type(e).__name__}: {e}"}
+
     base = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle on {args.cpu_heads or cfg.heads} heads", file=sys.stderr, flush=True)
@@ -365,8 +373,52 @@ def main():
         "backward": backward,
         "kpass": kpass,
         "block": block,
+        "graph": graphs,
     }
     print(json.dumps(line), flush=True)
+
+
+def graph_rates(sq, inputs, dev, iters=200):
+    """The forward of the two smallest configurations called eagerly through the
+    binding, back to back, against the same forward captured once in a HIP graph
+    and replayed: per-call time (ms) from HIP events.  With kernels of a few
+    microseconds the eager calls are bound by the host (argument checks, two
+    launches); a replay issues both kernels at once.  The replayed output equals
+    the eager one bit for bit."""
+    import torch
+
+    res = {}
+    for name in ("tiny_fp32", "small_bf16"):
+        cfg = inputs.CONFIGS[name]
+        q, k, v = (x.to(dev) for x in inputs.config_inputs(cfg))
+        out = torch.empty_like(q)
+        ws = torch.empty(sq.squad_attn_workspace_size(cfg.grid, cfg.tile, cfg.heads, cfg.batch, cfg.head_dim,
+                                                      cfg.dtype), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            sq.squad_attn_forward(q, k, v, cfg.grid, cfg.tile, cfg.heads, out=out, workspace=ws)
+
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fwd()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fwd()
+        stream = torch.cuda.current_stream(dev)
+        fwd()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        eager = time_launches(fwd, stream, iters)
+        replay = time_launches(g.replay, stream, iters)
+        torch.cuda.synchronize()
+        res[name] = {"eager_ms": round(eager, 4), "graph_replay_ms": round(replay, 4),
+                     "replay_equals_eager": bool(torch.equal(out, ref))}
+        del g
+    return res
 
 
 def permutation_rates(sq, cfg, q, stream):
