@@ -225,7 +225,10 @@ __device__ __forceinline__ float sum_halves(float x) {
 // - kPartWrite: written to outp as fp16 times a power of two 2^e per row, e chosen
 //   so that the row's largest magnitude lies in [2^14, 2^15) (e clamped to
 //   [-126, 126]), with 2^-e stored at scp[row]; kPartFinal: outp holds such a
-//   part, which is added (times scp[row]) before the sum is written as bf16 to outp.
+//   part, which is added (times scp[row]) before the sum is written as bf16 to outp;
+//   kPartAdd: the sum is written back as such a part, e chosen from the bound
+//   2^15 scp[row] + (the row's largest new magnitude) on the sum's magnitude (the
+//   row's owning lanes read the old scale before any lane writes the new one).
 // scp is indexed by the row's element offset / D (the scale array has one float
 // per head row of the tensor).  The rows pass through `stage` (32 rows x D / 2 fp32 =
 // 64 D bytes of LDS, the wave's own) half a row at a time and go out as whole row
@@ -241,16 +244,22 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], floa
   constexpr int MTR = D / 64;      // accumulator tiles per round
   constexpr int RPI = 64 / NCH;    // rows per store instruction
   const uint32_t half = lane >> 5, l32 = lane & 31;
-  const bool part = mode == kPartWrite || mode == kPartFinal;
-  // kPartWrite: this row's exponent e (lanes l32 and l32 + 32 agree)
+  const bool part = mode == kPartWrite || mode == kPartFinal || mode == kPartAdd;
+  // kPartWrite, kPartAdd: this row's exponent e (lanes l32 and l32 + 32 agree);
+  // kPartAdd also the old part's scale, read here by the row's owners
   int32_t e_row = 0;
-  if (mode == kPartWrite) {
+  float down_row = 0.f;
+  if (mode == kPartWrite || mode == kPartAdd) {
     float amax = 0.f;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[mt][r] * scale));
     amax = max_halves(amax);
+    if (mode == kPartAdd && off != kNoRow) {
+      down_row = scp[row_elems<WIDE, D>((int32_t)off) / D];
+      amax += 32768.f * down_row;   // the old part's magnitudes are below 2^15 times its scale
+    }
     // amax = f 2^k, f in [0.5, 1): amax 2^(15 - k) = f 2^15 lies in [2^14, 2^15)
     e_row = min(max(15 - __builtin_amdgcn_frexp_expf(amax), -126), 126);
   }
@@ -273,14 +282,20 @@ __device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], floa
       const uint32_t r = i * RPI + lane / NCH;
       const uint32_t o = (uint32_t)__shfl((int)off, (int)r, 64);
       const int32_t er = __shfl(e_row, (int)r, 64);
+      const float dold = __shfl(down_row, (int)r, 64);
       float4 x = *(const float4*)(stage + r * (DR * 4) + ((c ^ (r & (NCH - 1))) << 4));
       if (o != kNoRow) {
         const auto oe = row_elems<WIDE, D>((int32_t)o);
         const int d0 = DR * rd + 4 * c;
         if (part) {
           float* sp = scp + oe / D;
-          if (mode == kPartWrite) {
+          if (mode == kPartWrite || mode == kPartAdd) {
             const float up = __builtin_amdgcn_ldexpf(1.f, er);
+            if (mode == kPartAdd) {
+              const f16x4 y = *(const f16x4*)((const _Float16*)outp + oe + d0);
+              x.x = fmaf((float)y[0], dold, x.x); x.y = fmaf((float)y[1], dold, x.y);
+              x.z = fmaf((float)y[2], dold, x.z); x.w = fmaf((float)y[3], dold, x.w);
+            }
             f16x4 w;
             w[0] = (_Float16)(x.x * up); w[1] = (_Float16)(x.y * up);
             w[2] = (_Float16)(x.z * up); w[3] = (_Float16)(x.w * up);

@@ -914,15 +914,11 @@ KTrainLayout kpass_train_layout(const KGeo& kg, int32_t heads, int32_t batch, in
   t.dgrad[0] = al(t.dsum + rows * 4);
   t.dgrad[1] = t.dgrad[0] + t.one_g;
   size_t end = t.dgrad[1] + t.one_g;
-  // bf16: with a middle level the dq and dk parts are summed in fp32 accumulators;
-  // with two levels the first level's parts travel in dq and dk as scaled fp16
-  // rows, as in squad_attn_backward (one inverse scale per head row)
+  // bf16: the levels' dq and dk parts travel in dq and dk as scaled fp16 rows, as
+  // in squad_attn_backward (one inverse scale per head row); the middle levels add
+  // to them
   t.dq_acc = t.dk_acc = t.dq_sc = t.dk_sc = 0;
-  if (bf16 && kg.k > 2) {
-    t.dq_acc = end;
-    t.dk_acc = al(t.dq_acc + rows * head_dim * 4);
-    end = al(t.dk_acc + rows * head_dim * 4);
-  } else if (bf16) {
+  if (bf16) {
     t.dq_sc = end;
     t.dk_sc = al(t.dq_sc + rows * 4);
     end = al(t.dk_sc + rows * 4);
@@ -1045,7 +1041,7 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = dtype == SQUAD_DTYPE_BF16;
   const size_t rows = (size_t)heads * batch * kg.n;
-  const bool parts = bf16 && levels == 2;   // the fp16 part hand-off of two passes
+  const bool parts = bf16;   // the fp16 part hand-off between the levels
   float* dq_acc = parts ? nullptr : bf16 ? (float*)(ws + t.dq_acc) : (float*)dq;
   float* dk_acc = parts ? nullptr : bf16 ? (float*)(ws + t.dk_acc) : (float*)dk;
   float* dq_sc = parts ? (float*)(ws + t.dq_sc) : nullptr;
@@ -1059,7 +1055,7 @@ int squad_kpass_backward(const void* q, const void* k, const void* v, const void
     const void* outj = j == levels - 1 ? out : inter(j + 1);
     const void* up = j == levels - 1 ? dout : ws + t.dgrad[(j + 1) & 1];
     void* dvj = j == 0 ? dv : ws + t.dgrad[j & 1];
-    const uint32_t mode = parts ? (j == 1 ? kPartWrite : kPartFinal)
+    const uint32_t mode = parts ? (j == levels - 1 ? kPartWrite : (j == 0 ? kPartFinal : kPartAdd))
                                 : j == levels - 1 ? kAccWrite : (j == 0 ? kAccFinal : kAccAdd);
     auto fill = [&](auto& a) {
       kpass_bwd_common(a, kg, j, heads, batch, head_dim, scale);

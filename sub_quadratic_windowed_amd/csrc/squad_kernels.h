@@ -92,9 +92,11 @@ hipError_t launch_attn_f32_k(AttnArgsK a, int head_dim, hipStream_t stream);
 // writes dq / dk in the call's dtype (for fp32 calls the accumulators are dq and dk
 // themselves).  The two-pass bf16 backward hands the global pass's dq and dk parts to the local
 // pass in the dq and dk buffers themselves, as fp16 rows scaled by a power of two
-// per row (the scale's inverse in dq_sc / dk_sc): kPartWrite writes them, kPartFinal
-// adds them and writes the bf16 gradients.
-enum BwdAcc : uint32_t { kAccWrite = 0, kAccFinal = 1, kAccAdd = 2, kPartWrite = 3, kPartFinal = 4 };
+// per row (the scale's inverse in dq_sc / dk_sc): kPartWrite writes them, kPartAdd
+// (middle levels of k levels) adds to them, kPartFinal adds them and writes the
+// bf16 gradients.
+enum BwdAcc : uint32_t { kAccWrite = 0, kAccFinal = 1, kAccAdd = 2, kPartWrite = 3, kPartFinal = 4,
+                         kPartAdd = 5 };
 template <typename Map>
 struct BwdArgsT {
   const void* q;

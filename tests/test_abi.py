@@ -472,8 +472,9 @@ def test_kpass_training_argument_checks():
     p = ctypes.c_void_p
     assert sq.squad_kpass_train_workspace_size((4, 8, 8), [(1, 4, 4), (2, 2, 8)], 2, 1, 64, 1) == 0   # not nested
     need = sq.squad_kpass_train_workspace_size((4, 8, 8), [(1, 2, 2), (2, 4, 4)], 2, 1, 64, 1)
-    # two fp16 intermediates, three levels of statistics, D, two gradient buffers, two fp32 sums
-    assert need >= 2 * 256 * 2 * 64 * 2 + 4 * 256 * 2 * 4 + 2 * 256 * 2 * 64 * 2 + 2 * 256 * 2 * 64 * 4
+    # two fp16 intermediates, three levels of statistics, D, two gradient buffers, and
+    # one inverse scale per head row of dq and of dk
+    assert need == 2 * 256 * 2 * 64 * 2 + 4 * 256 * 2 * 4 + 2 * 256 * 2 * 64 * 2 + 2 * 256 * 2 * 4
     arr = (ctypes.c_int32 * 6)(1, 2, 2, 2, 4, 4)
     g = _lib.int3((4, 8, 8))
     D, K, V, OUT, DOUT = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
